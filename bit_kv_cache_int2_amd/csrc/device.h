@@ -1,0 +1,94 @@
+// Device helpers shared by the kvint2 kernels (gfx950, wave64).
+//
+// Number formats follow the contract in include/kvint2.h: IEEE fp32 with
+// round-to-nearest-even, no contraction (the library is built with
+// -ffp-contract=off; every fused multiply-add is written as fmaf), fp16
+// conversions by v_cvt_f16_f32 / v_cvt_f32_f16 in the default RNE mode with
+// denormals kept.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define KVQ_DEV __device__ __forceinline__
+
+namespace kvq {
+
+constexpr int kGroup = 32;
+constexpr int kWindow = 64;
+constexpr int kWave = 64;
+
+KVQ_DEV float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Pins x as an fp32 value in a register.  Without it the backend may fuse
+// the producing fma with a following fp16 conversion (v_fma_mix*_f16), which
+// rounds once from the exact value instead of to fp32 and then to fp16.
+KVQ_DEV float opaque(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+KVQ_DEV uint32_t f32_to_f16_bits(float x) {
+  _Float16 h = (_Float16)opaque(x);
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+KVQ_DEV float f16_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(b & 0xFFFFu));
+}
+
+// Unpack 8 bf16 held in a uint4 into fp32, canonicalising -0 to +0.
+KVQ_DEV void bf16x8_to_f32(const uint4 u, float* x) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16) + 0.0f;
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u) + 0.0f;
+  }
+}
+
+// The INT2 group quantizer's parameters for a group with extrema mn, mx
+// (canonical inputs).  t0..t2 are the three decision thresholds; when the
+// stored scale is 0 they are +inf so that every code is 0.
+struct Q2 {
+  float s, z, t0, t1, t2;
+  uint32_t word;  // fp16 scale bits | fp16 zero bits << 16
+};
+
+KVQ_DEV Q2 q2_make(float mn, float mx) {
+  Q2 q;
+  const float s32 = (mx - mn) / 3.0f;
+  const uint32_t sh = f32_to_f16_bits(s32), zh = f32_to_f16_bits(mn);
+  q.s = f16_bits_to_f32(sh);
+  q.z = f16_bits_to_f32(zh);
+  q.word = sh | (zh << 16);
+  const bool zero = (q.s == 0.0f);
+  q.t0 = zero ? __builtin_inff() : __builtin_fmaf(0.5f, q.s, q.z);
+  q.t1 = zero ? __builtin_inff() : __builtin_fmaf(1.5f, q.s, q.z);
+  q.t2 = zero ? __builtin_inff() : __builtin_fmaf(2.5f, q.s, q.z);
+  return q;
+}
+
+KVQ_DEV uint32_t q2_code(float x, const Q2& q) {
+  return (uint32_t)(x >= q.t0) + (uint32_t)(x >= q.t1) + (uint32_t)(x >= q.t2);
+}
+
+// Wave-level reductions (64 lanes) with butterfly shuffles.
+KVQ_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+KVQ_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// fp32 value of byte b (0..3) of x, exact for 0..255 (v_cvt_f32_ubyteN).
+template <int B>
+KVQ_DEV float ubyte_f32(uint32_t x) {
+  return (float)((x >> (8 * B)) & 0xFFu);
+}
+
+}  // namespace kvq

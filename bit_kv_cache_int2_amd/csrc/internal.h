@@ -1,0 +1,36 @@
+// Host-side launcher interface between the C ABI (api.cpp) and the kernel
+// translation units.  Arguments reaching these functions have already been
+// validated by api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "kvint2.h"
+
+namespace kvq {
+
+hipError_t launch_quantize_append(const kvq_cache* c, const void* k_bf16,
+                                  const void* v_bf16, int cur_len, int n_new,
+                                  hipStream_t stream);
+
+hipError_t launch_cluster_assign(const void* keys, int64_t n, int head_dim,
+                                 int64_t key_stride, const float* centroids,
+                                 int n_centroids, const float* sens_w, int topk,
+                                 int32_t* idx_out, hipStream_t stream);
+
+// Number of token splits the decode uses, and the workspace they need.
+int decode_splits(const kvq_layout* L, int q_heads, int n_tokens);
+size_t decode_workspace_bytes(const kvq_layout* L, int q_heads, int n_tokens);
+
+hipError_t launch_decode(const kvq_cache* c, int n_tokens, const void* q,
+                         int q_dtype, int q_heads, float scale, void* out,
+                         int out_dtype, float* lse, void* ws, hipStream_t stream);
+
+size_t chunk_workspace_bytes(const kvq_layout* L, int q_len, int q_heads,
+                             int n_tokens);
+
+hipError_t launch_chunk(const kvq_cache* c, int n_tokens, const void* q,
+                        int q_len, int q_heads, float scale, void* out,
+                        int out_dtype, float* lse, void* ws, hipStream_t stream);
+
+}  // namespace kvq

@@ -1,0 +1,128 @@
+"""The C-ABI library loads, exports every function include/kvint2.h
+declares, and its host-side validation rejects bad arguments before any
+launch.  No call here reaches the GPU (validation fails first), so this runs
+on machines without one."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_kv_cache_int2_amd as kv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvint2.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_four_entry_points():
+    names = _declared_functions()
+    for n in ("kv_quantize_append", "kv_cluster_assign", "attn_int2_decode", "attn_int2_chunk"):
+        assert n in names
+    assert len(names) >= 9
+
+
+def test_library_exports_every_declared_symbol():
+    L = kv.lib()
+    for n in _declared_functions():
+        assert hasattr(L, n), n
+    assert L.kvq_status_string(-3) == b"exceeds cache capacity"
+
+
+def _layout(**kw):
+    d = dict(batch=2, kv_heads=4, head_dim=128, capacity=1024, key_mode=kv.KEY_WINDOW,
+             value_mode=kv.VAL_GROUP, n_centroids=0, qsac_topk=1, psac_rank=0)
+    d.update(kw)
+    return kv.Layout(*[d[f] for f, _ in kv.Layout._fields_])
+
+
+def test_layout_validation():
+    chk = lambda **kw: kv.lib().kvq_layout_check(ctypes.byref(_layout(**kw)))
+    assert chk() == kv.KVQ_OK
+    assert chk(capacity=1000) == kv.KVQ_EINVAL
+    assert chk(batch=0) == kv.KVQ_EINVAL
+    assert chk(head_dim=96) == kv.KVQ_EUNSUPPORTED
+    assert chk(key_mode=7) == kv.KVQ_EINVAL
+    assert chk(key_mode=kv.KEY_CENTROID, n_centroids=0) == kv.KVQ_EUNSUPPORTED
+    assert chk(key_mode=kv.KEY_CENTROID, n_centroids=300) == kv.KVQ_EUNSUPPORTED
+    assert chk(key_mode=kv.KEY_CENTROID, n_centroids=16, psac_rank=8) == kv.KVQ_OK
+    assert chk(key_mode=kv.KEY_CENTROID, n_centroids=16, psac_rank=4) == kv.KVQ_EUNSUPPORTED
+    assert chk(psac_rank=8) == kv.KVQ_EUNSUPPORTED
+    assert chk(key_mode=kv.KEY_CENTROID_QSAC, n_centroids=16, qsac_topk=9) == kv.KVQ_EINVAL
+    assert chk(key_mode=kv.KEY_CENTROID_QSAC, n_centroids=2, qsac_topk=4) == kv.KVQ_EINVAL
+
+
+def test_buffer_sizes():
+    L = _layout()
+    nb = lambda w: kv.lib().kvq_buffer_bytes(ctypes.byref(L), w)
+    BH, T, D = 8, 1024, 128
+    assert nb(0) == BH * T * D // 4                # k_codes
+    assert nb(1) == BH * (T // 64) * D * 4         # window params
+    assert nb(2) == BH * 64 * D * 2                # tail
+    assert nb(3) == 0 and nb(4) == 0 and nb(7) == 0
+    assert nb(8) == BH * T * D // 4 and nb(9) == BH * T * (D // 32) * 4
+    L = _layout(key_mode=kv.KEY_CENTROID_QSAC, n_centroids=256, qsac_topk=4, psac_rank=8)
+    assert nb(1) == BH * T * (D // 32) * 4
+    assert nb(2) == 0 and nb(3) == BH * T and nb(4) == BH * 256 * D * 4
+    assert nb(5) == BH * D * 4 and nb(6) == BH * D * 8 * 4 and nb(7) == BH * T * 8 * 2
+    assert nb(99) == 0
+
+
+def _cache(**kw):
+    L = _layout(**kw)
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced: validation fails first
+    return kv.CacheStruct(L, *[fake] * len(kv.BUFFERS))
+
+
+def test_append_validation_without_launch():
+    L = kv.lib()
+    c = _cache()
+    p = ctypes.c_void_p(1 << 20)
+    assert L.kv_quantize_append(None, p, p, 0, 1, None) == kv.KVQ_EINVAL
+    assert L.kv_quantize_append(ctypes.byref(c), p, p, -1, 1, None) == kv.KVQ_EINVAL
+    assert L.kv_quantize_append(ctypes.byref(c), p, p, 1000, 25, None) == kv.KVQ_ECAPACITY
+    assert L.kv_quantize_append(ctypes.byref(c), None, p, 0, 1, None) == kv.KVQ_EINVAL
+    assert L.kv_quantize_append(ctypes.byref(c), p, p, 5, 0, None) == kv.KVQ_OK   # no-op
+    bad = _cache()
+    bad.v_codes = None
+    assert L.kv_quantize_append(ctypes.byref(bad), p, p, 0, 1, None) == kv.KVQ_EINVAL
+    mis = _cache()
+    mis.k_codes = ctypes.c_void_p((1 << 20) + 4)
+    assert L.kv_quantize_append(ctypes.byref(mis), p, p, 0, 1, None) == kv.KVQ_EINVAL
+
+
+def test_attention_validation_without_launch():
+    L = kv.lib()
+    c = _cache()
+    p = ctypes.c_void_p(1 << 20)
+    call = lambda n=100, hq=8, od=kv.F32, ws=p, wsb=1 << 30, qd=kv.F32: L.attn_int2_decode(
+        ctypes.byref(c), n, p, qd, hq, 0.1, p, od, None, ws, wsb, None)
+    assert call(hq=6) == kv.KVQ_EINVAL
+    assert call(hq=4 * 3) == kv.KVQ_EUNSUPPORTED
+    assert call(n=0) == kv.KVQ_EINVAL
+    assert call(n=2000) == kv.KVQ_ECAPACITY
+    assert call(od=7) == kv.KVQ_EINVAL
+    assert call(qd=9) == kv.KVQ_EINVAL
+    assert call(wsb=16) == kv.KVQ_EWORKSPACE
+    assert call(ws=None) == kv.KVQ_EWORKSPACE
+    need = L.attn_int2_decode_workspace(ctypes.byref(c.layout), 8, 100)
+    assert need > 0 and need % 4 == 0
+    assert L.attn_int2_chunk(ctypes.byref(c), 100, p, 0, 8, 0.1, p, kv.F32, None, p, 1 << 30,
+                             None) == kv.KVQ_EINVAL
+
+
+def test_assign_validation_without_launch():
+    L = kv.lib()
+    p = ctypes.c_void_p(1 << 20)
+    assert L.kv_cluster_assign(p, -1, 128, 128, p, 16, None, 1, p, None) == kv.KVQ_EINVAL
+    assert L.kv_cluster_assign(p, 10, 96, 96, p, 16, None, 1, p, None) == kv.KVQ_EUNSUPPORTED
+    assert L.kv_cluster_assign(p, 10, 128, 128, p, 0, None, 1, p, None) == kv.KVQ_EUNSUPPORTED
+    assert L.kv_cluster_assign(p, 10, 128, 100, p, 16, None, 1, p, None) == kv.KVQ_EINVAL
+    assert L.kv_cluster_assign(p, 10, 128, 128, p, 16, p, 9, p, None) == kv.KVQ_EINVAL
+    assert L.kv_cluster_assign(p, 0, 128, 128, p, 16, None, 1, p, None) == kv.KVQ_OK

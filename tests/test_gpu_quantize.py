@@ -1,0 +1,111 @@
+"""GPU parity of kv_quantize_append and kv_cluster_assign against the
+oracle: packed codes, parameter words, the bf16 tail, centroid indices and
+PSAC words must be bit-identical."""
+import numpy as np
+import pytest
+import torch
+
+import bit_kv_cache_int2_amd as kv
+import oracle
+import synth
+from gpu_helpers import assert_cache_equal, calibrate, dev_bf16, oracle_like, to_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _append_both(c, o, K, V, chunks):
+    pos = 0
+    for n in chunks:
+        k = np.ascontiguousarray(K[:, pos:pos + n])
+        v = np.ascontiguousarray(V[:, pos:pos + n])
+        kv.kv_quantize_append(c, dev_bf16(k), dev_bf16(v), pos)
+        o.append(k, v, pos)
+        pos += n
+    torch.cuda.synchronize()
+    return pos
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("chunks", [[1000], [1, 7, 56, 64, 100, 500, 272], [63, 1, 64, 65, 807]])
+def test_window_keys_and_values(D, chunks):
+    d = synth.llm_decode(B=2, Hkv=3, Hq=6, D=D, T=1000)
+    c = kv.KVCache(2, 3, D, 1024)
+    o = oracle_like(c)
+    n = _append_both(c, o, d["K"], d["V"], chunks)
+    assert_cache_equal(to_oracle(c), o, n, f"D={D} chunks={chunks}")
+
+
+def test_window_keys_chunked_equals_one_shot_on_gpu():
+    d = synth.llm_decode(B=1, Hkv=2, Hq=2, D=128, T=2000)
+    a = kv.KVCache(1, 2, 128, 2048)
+    b = kv.KVCache(1, 2, 128, 2048)
+    kv.kv_quantize_append(a, dev_bf16(d["K"]), dev_bf16(d["V"]), 0)
+    pos = 0
+    for n in [1560 - 1500, 1, 1499, 440]:
+        kv.kv_quantize_append(b, dev_bf16(d["K"][:, pos:pos + n]), dev_bf16(d["V"][:, pos:pos + n]), pos)
+        pos += n
+    torch.cuda.synchronize()
+    assert_cache_equal(to_oracle(a), to_oracle(b), 2000, "one-shot vs chunked")
+
+
+@pytest.mark.parametrize("hadamard", [False, True])
+def test_toy_centroid_keys(hadamard):
+    d = synth.toy_single_head()
+    c = kv.KVCache(1, 1, 64, 512, key_mode=kv.KEY_CENTROID, n_centroids=16,
+                   value_mode=kv.VAL_HADAMARD if hadamard else kv.VAL_GROUP)
+    calibrate(c, d["K"], d["kmeans_init"], 4)
+    o = oracle_like(c)
+    n = _append_both(c, o, d["K"], d["V"], [512])
+    assert_cache_equal(to_oracle(c), o, n, "toy")
+
+
+@pytest.mark.parametrize("mode,R", [(kv.KEY_CENTROID, 0), (kv.KEY_CENTROID, 8),
+                                    (kv.KEY_CENTROID_QSAC, 0), (kv.KEY_CENTROID_QSAC, 8)])
+def test_centroid_qsac_psac_hadamard(mode, R):
+    d = synth.sensitivity_aware(H=2, T=700, Lq=8, C=32, n_cal=256)
+    c = kv.KVCache(1, 2, 128, 768, key_mode=mode, value_mode=kv.VAL_HADAMARD, n_centroids=32,
+                   qsac_topk=4, psac_rank=R)
+    calibrate(c, d["K"], d["kmeans_init"][:, :, :32], 2, d["q_cal"])
+    o = oracle_like(c)
+    n = _append_both(c, o, d["K"], d["V"], [300, 1, 399])
+    assert_cache_equal(to_oracle(c), o, n, f"mode={mode} R={R}")
+
+
+def test_cluster_assign_plain_and_qsac():
+    rng = np.random.default_rng(3)
+    C, D, n = 200, 128, 3000
+    cent = rng.standard_normal((C, D)).astype(np.float32)
+    cent[150] = cent[17]                                  # duplicate: lower index wins
+    keys = synth.to_bf16_bits(cent[rng.integers(0, C, n)] + 0.9 * rng.standard_normal((n, D)))
+    keys[5] = synth.to_bf16_bits(cent[17])                # exact hit of a duplicated centroid
+    w = rng.uniform(0.2, 2.0, D).astype(np.float32)
+    # rows strided inside a wider matrix
+    wide = np.zeros((n, 3 * D), np.uint16)
+    wide[:, D:2 * D] = keys
+    kt = dev_bf16(wide)[:, D:2 * D]
+    ct = torch.from_numpy(cent).cuda()
+    got = kv.kv_cluster_assign(kt, ct).cpu().numpy()
+    gq = kv.kv_cluster_assign(kt, ct, torch.from_numpy(w).cuda(), topk=4).cpu().numpy()
+    kf = synth.bf16_bits_to_f32(keys)
+    want = np.array([oracle.assign_plain(kf[i], cent) for i in range(n)])
+    wq = np.array([oracle.assign_qsac(kf[i], cent, w, 4) for i in range(n)])
+    assert np.array_equal(got, want)
+    assert np.array_equal(gq, wq)
+    assert got[5] == 17
+
+
+@pytest.mark.slow
+def test_llm_decode_build_full_size_sampled():
+    """Full 16 x 32768 x 8-head window-key build (the benchmark's launch
+    configuration); all bytes of sampled (sequence, head) pairs compared."""
+    d = synth.llm_decode()
+    B, H, T = d["B"], d["Hkv"], d["T"]
+    c = kv.KVCache(B, H, 128, T)
+    kv.kv_quantize_append(c, dev_bf16(d["K"]), dev_bf16(d["V"]), 0)
+    torch.cuda.synchronize()
+    g = to_oracle(c)
+    for b, h in [(0, 0), (7, 3), (15, 7), (11, 5)]:
+        o = oracle.Cache(1, 1, 128, T)
+        o.append(np.ascontiguousarray(d["K"][b:b + 1, :, h:h + 1]),
+                 np.ascontiguousarray(d["V"][b:b + 1, :, h:h + 1]), 0)
+        assert_cache_equal(g.slice_bh(b, h), o, T, f"b={b} h={h}")
