@@ -56,26 +56,15 @@ KVQ_DEV void wht_row(float (&x)[8]) {
   for (int k = 0; k < 8; ++k) x[k] = x[k] * c + 0.0f;
 }
 
+// Quantise the 8-channel slice this lane holds of one token row (a row is
+// spread over D/8 consecutive lanes, so every lane of the row must take
+// part; `ok` false lanes only join the shuffles).
 template <int D, bool HAD>
-__global__ __launch_bounds__(256) void quant_values_kernel(
-    const uint16_t* __restrict__ vin, uint8_t* __restrict__ vcodes,
-    uint32_t* __restrict__ vparams, int H, int Tcap, int cur_len, int n_new,
-    int64_t rows) {
-  constexpr int LPR = D / 8;
-  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gt / LPR;  // (b, h, i) with i fastest
-  const int j = threadIdx.x & (LPR - 1);
-  const bool ok = row < rows;
-  int64_t i = 0, bh = 0, b = 0, h = 0;
+KVQ_DEV void value_slice(const uint16_t* src, bool ok, int j, uint8_t* code_row,
+                         uint32_t* prm_row) {
   float x[8];
   if (ok) {
-    i = row % n_new;
-    bh = row / n_new;
-    h = bh % H;
-    b = bh / H;
-    const uint4 u = *reinterpret_cast<const uint4*>(
-        vin + ((b * n_new + i) * H + h) * D + j * 8);
-    bf16x8_to_f32(u, x);
+    bf16x8_to_f32(*reinterpret_cast<const uint4*>(src + j * 8), x);
   } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k) x[k] = 0.0f;
@@ -96,49 +85,79 @@ __global__ __launch_bounds__(256) void quant_values_kernel(
 #pragma unroll
   for (int k = 0; k < 8; ++k) bits |= q2_code(x[k], q) << (2 * k);
   if (ok) {
-    const int64_t orow = bh * Tcap + cur_len + i;
-    *reinterpret_cast<uint16_t*>(vcodes + orow * (D / 4) + j * 2) = (uint16_t)bits;
-    if ((j & 3) == 0) vparams[orow * (D / kGroup) + (j >> 2)] = q.word;
+    *reinterpret_cast<uint16_t*>(code_row + j * 2) = (uint16_t)bits;
+    if ((j & 3) == 0) prm_row[j >> 2] = q.word;
   }
 }
 
+// Values only (centroid-key modes): rows (b, h, i) with i fastest.
+template <int D, bool HAD>
+__global__ __launch_bounds__(256) void quant_values_kernel(
+    const uint16_t* __restrict__ vin, uint8_t* __restrict__ vcodes,
+    uint32_t* __restrict__ vparams, int H, int Tcap, int cur_len, int n_new,
+    int64_t rows) {
+  constexpr int LPR = D / 8;
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
+  const int j = threadIdx.x & (LPR - 1);
+  const bool ok = row < rows;
+  const int64_t i = ok ? row % n_new : 0, bh = ok ? row / n_new : 0;
+  const int64_t h = bh % H, b = bh / H;
+  const int64_t orow = bh * Tcap + cur_len + i;
+  value_slice<D, HAD>(vin + ((b * n_new + i) * H + h) * D, ok, j, vcodes + orow * (D / 4),
+                      vparams + orow * (D / kGroup));
+}
+
 // ---------------------------------------------------------------- window keys
-template <int D>
-__global__ __launch_bounds__(256) void quant_key_windows_kernel(
-    const uint16_t* __restrict__ kin, uint8_t* __restrict__ kcodes,
-    uint32_t* __restrict__ kparams, uint16_t* __restrict__ ktail, int H,
-    int Tcap, int cur_len, int n_new, int n_win) {
-  constexpr int PARTS = 256 / D;          // threads per channel
-  constexpr int TPP = kWindow / PARTS;    // tokens per thread
-  __shared__ float tile[kWindow][D + 1];
-  __shared__ uint8_t codes[kWindow][D];
+// One block per (64-token window touched by the append, head, sequence):
+// the window's new value rows, then -- if the append completes the window --
+// its keys, quantised per channel over the 64 tokens (old tokens from the
+// tail, new ones from the input).  Block 0 also writes the tokens of the
+// window left unfinished into the tail, after its own reads of the old tail.
+template <int D, bool HAD>
+__global__ __launch_bounds__(256) void window_append_kernel(
+    const uint16_t* __restrict__ kin, const uint16_t* __restrict__ vin,
+    uint8_t* __restrict__ kcodes, uint32_t* __restrict__ kparams,
+    uint16_t* __restrict__ ktail, uint8_t* __restrict__ vcodes,
+    uint32_t* __restrict__ vparams, int H, int Tcap, int cur_len, int n_new) {
+  constexpr int LPR = D / 8, RPP = 256 / LPR;  // lanes per row, rows per pass
+  constexpr int PARTS = 256 / D;              // threads per channel
+  constexpr int TPP = kWindow / PARTS;        // tokens per thread
+  __shared__ __align__(16) uint16_t tile[kWindow][D + 8];
+  __shared__ __align__(16) uint8_t codes[kWindow][D];
   __shared__ float red_mn[PARTS][D], red_mx[PARTS][D];
 
   const int job = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = (int64_t)b * H + h;
   const int end = cur_len + n_new;
   const int tid = threadIdx.x;
+  const int w = cur_len / kWindow + job;
+  const int t_lo = max(w * kWindow, cur_len), t_hi = min(w * kWindow + kWindow, end);
   const uint16_t* tail = ktail + bh * kWindow * D;
 
-  if (job < n_win) {
-    const int w = cur_len / kWindow + job;
+  for (int base = t_lo; base < t_hi; base += RPP) {
+    const int t = base + tid / LPR;
+    const bool ok = t < t_hi;
+    const int64_t orow = bh * Tcap + (ok ? t : t_lo);
+    value_slice<D, HAD>(vin + (((int64_t)b * n_new + (t - cur_len)) * H + h) * D, ok,
+                        tid % LPR, vcodes + orow * (D / 4), vparams + orow * (D / kGroup));
+  }
+
+  if (w * kWindow + kWindow <= end) {
     for (int e = tid; e < kWindow * D / 8; e += 256) {
       const int t = e / (D / 8), jj = e % (D / 8);
       const int p = w * kWindow + t;
       const uint16_t* src =
           (p < cur_len) ? tail + (int64_t)(p & (kWindow - 1)) * D
                         : kin + (((int64_t)b * n_new + (p - cur_len)) * H + h) * D;
-      float x[8];
-      bf16x8_to_f32(*reinterpret_cast<const uint4*>(src + jj * 8), x);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) tile[t][jj * 8 + k] = x[k];
+      *reinterpret_cast<uint4*>(&tile[t][jj * 8]) = *reinterpret_cast<const uint4*>(src + jj * 8);
     }
     __syncthreads();
     const int c = tid % D, part = tid / D;
-    float mn = tile[part * TPP][c], mx = mn;
+    float mn = bf16_to_f32(tile[part * TPP][c]) + 0.0f, mx = mn;
     for (int t = part * TPP + 1; t < (part + 1) * TPP; ++t) {
-      mn = fminf(mn, tile[t][c]);
-      mx = fmaxf(mx, tile[t][c]);
+      const float x = bf16_to_f32(tile[t][c]) + 0.0f;
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
     }
     red_mn[part][c] = mn;
     red_mx[part][c] = mx;
@@ -150,7 +169,7 @@ __global__ __launch_bounds__(256) void quant_key_windows_kernel(
     }
     const Q2 q = q2_make(mn, mx);
     for (int t = part * TPP; t < (part + 1) * TPP; ++t)
-      codes[t][c] = (uint8_t)q2_code(tile[t][c], q);
+      codes[t][c] = (uint8_t)q2_code(bf16_to_f32(tile[t][c]) + 0.0f, q);
     if (part == 0) kparams[(bh * (Tcap / kWindow) + w) * D + c] = q.word;
     __syncthreads();
     // pack: each thread emits 8 bytes (32 codes) of one token row
@@ -162,7 +181,7 @@ __global__ __launch_bounds__(256) void quant_key_windows_kernel(
       uint32_t outw[2] = {0u, 0u};
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        // 4 one-byte codes -> one packed byte
+        // four one-byte codes -> one packed byte
         const uint32_t v = in[k];
         const uint32_t byte = (v & 3u) | ((v >> 6) & 0xCu) | ((v >> 12) & 0x30u) | ((v >> 18) & 0xC0u);
         outw[k >> 2] |= byte << (8 * (k & 3));
@@ -400,15 +419,20 @@ hipError_t launch_values(const kvq_cache* c, const void* v, int cur_len, int n_n
 }
 
 template <int D>
-hipError_t launch_key_windows(const kvq_cache* c, const void* k, int cur_len, int n_new,
-                              hipStream_t st) {
+hipError_t launch_window_append(const kvq_cache* c, const void* k, const void* v, int cur_len,
+                                int n_new, hipStream_t st) {
   const kvq_layout& L = c->layout;
   const int end = cur_len + n_new;
-  const int n_win = end / kWindow - cur_len / kWindow;
-  const dim3 grid((unsigned)(n_win > 0 ? n_win : 1), (unsigned)L.kv_heads, (unsigned)L.batch);
-  quant_key_windows_kernel<D><<<grid, 256, 0, st>>>(
-      (const uint16_t*)k, (uint8_t*)c->k_codes, (uint32_t*)c->k_params,
-      (uint16_t*)c->k_tail, L.kv_heads, L.capacity, cur_len, n_new, n_win);
+  const int jobs = (end - 1) / kWindow - cur_len / kWindow + 1;
+  const dim3 grid((unsigned)jobs, (unsigned)L.kv_heads, (unsigned)L.batch);
+  auto args = [&](auto kern) {
+    kern<<<grid, 256, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, (uint8_t*)c->k_codes,
+                               (uint32_t*)c->k_params, (uint16_t*)c->k_tail,
+                               (uint8_t*)c->v_codes, (uint32_t*)c->v_params, L.kv_heads,
+                               L.capacity, cur_len, n_new);
+  };
+  if (L.value_mode == KVQ_VAL_HADAMARD) args(window_append_kernel<D, true>);
+  else args(window_append_kernel<D, false>);
   return hipGetLastError();
 }
 
@@ -426,10 +450,12 @@ hipError_t launch_centroid_cache(const kvq_cache* c, const void* k, int cur_len,
 }
 
 template <int D>
-hipError_t launch_keys(const kvq_cache* c, const void* k, int cur_len, int n_new,
-                       hipStream_t st) {
+hipError_t launch_append(const kvq_cache* c, const void* k, const void* v, int cur_len,
+                         int n_new, hipStream_t st) {
   const kvq_layout& L = c->layout;
-  if (L.key_mode == KVQ_KEY_WINDOW) return launch_key_windows<D>(c, k, cur_len, n_new, st);
+  if (L.key_mode == KVQ_KEY_WINDOW) return launch_window_append<D>(c, k, v, cur_len, n_new, st);
+  hipError_t e = launch_values<D>(c, v, cur_len, n_new, st);
+  if (e != hipSuccess) return e;
   const bool qsac = L.key_mode == KVQ_KEY_CENTROID_QSAC;
   if (L.psac_rank == 8)
     return qsac ? launch_centroid_cache<D, true, 8>(c, k, cur_len, n_new, st)
@@ -454,12 +480,8 @@ hipError_t launch_quantize_append(const kvq_cache* c, const void* k_bf16,
                                   const void* v_bf16, int cur_len, int n_new,
                                   hipStream_t stream) {
   if (n_new == 0) return hipSuccess;
-  const int D = c->layout.head_dim;
-  hipError_t e = (D == 128) ? launch_values<128>(c, v_bf16, cur_len, n_new, stream)
-                            : launch_values<64>(c, v_bf16, cur_len, n_new, stream);
-  if (e != hipSuccess) return e;
-  return (D == 128) ? launch_keys<128>(c, k_bf16, cur_len, n_new, stream)
-                    : launch_keys<64>(c, k_bf16, cur_len, n_new, stream);
+  return (c->layout.head_dim == 128) ? launch_append<128>(c, k_bf16, v_bf16, cur_len, n_new, stream)
+                                     : launch_append<64>(c, k_bf16, v_bf16, cur_len, n_new, stream);
 }
 
 hipError_t launch_cluster_assign(const void* keys, int64_t n, int head_dim,

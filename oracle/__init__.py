@@ -74,6 +74,8 @@ def lib():
     L.orc_sens_weights.restype = None
     L.orc_pca.argtypes = [vp, i32, i32, i32, vp, vp]
     L.orc_pca.restype = i32
+    L.orc_num_threads.argtypes = []
+    L.orc_num_threads.restype = i32
     _lib = L
     return L
 
@@ -83,6 +85,10 @@ def _p(a):
         return None
     assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"], "need C-contiguous numpy"
     return ctypes.c_void_p(a.ctypes.data)
+
+
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
 
 
 # ---------------------------------------------------------------- scalars

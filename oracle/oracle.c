@@ -24,6 +24,7 @@
  */
 #include <float.h>
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -33,6 +34,9 @@
 
 enum { KEY_WINDOW = 0, KEY_CENTROID = 1, KEY_CENTROID_QSAC = 2 };
 enum { VAL_GROUP = 0, VAL_HADAMARD = 1 };
+
+/* OpenMP threads the oracle's parallel loops may use. */
+int orc_num_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------ */
 /* Number formats                                                      */
