@@ -16,6 +16,13 @@ region.  Per-call times come from HIP events on the stream the library
 launches on.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+Other workloads (measurement of the chunk-attention path; not the default
+line): --workload long_history | video_chunk | sensitivity.  Their step is
+the chunk attention of a query frame (or frames) against the packed history
+plus, for long_history and video_chunk, the quantize-append of that
+frame's own keys and values; `value` is then the attention's algorithmic
+TFLOP/s (4 * q_len * n_tokens * head_dim * heads per call).
 """
 from __future__ import annotations
 
@@ -105,17 +112,124 @@ def cpu_baseline(d) -> dict:
                       f"attention, {dt:.2f} s"}
 
 
+MFMA_PEAK_TFS = 2500.0        # MI355X dense fp16 MFMA, vendor figure
+
+
+def chunk_workload(name: str, steps: int, warmup: int) -> dict:
+    """Chunk-attention workloads (40 heads, head_dim 128)."""
+    import numpy as np
+    import torch
+
+    import bit_kv_cache_int2_amd as kv
+    import synth
+
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    if name == "long_history":
+        d = synth.long_history()
+        H, T, Lq = d["Hkv"], d["T"], d["Lq"]
+        cache = kv.KVCache(1, H, D, ((T + Lq + 63) // 64) * 64)
+        desc = {"workload": "long_history", "heads": H, "head_dim": D, "context": T, "q_len": Lq,
+                "keys": "int2 per channel, 64-token windows + bf16 tail",
+                "values": "int2 per token, groups of 32", "append_per_step": Lq}
+    elif name == "video_chunk":
+        d = synth.video_chunk()
+        H, T, Lq = d["Hkv"], d["T"], d["Lq"]
+        cache = kv.KVCache(1, H, D, ((T + Lq + 63) // 64) * 64, key_mode=kv.KEY_CENTROID,
+                           n_centroids=256, value_mode=kv.VAL_HADAMARD)
+        K = synth.bf16_bits_to_f32(d["K"])[0]
+        cent = np.stack([K[d["kmeans_init"][0, h], h] for h in range(H)])[None]
+        cache.centroids.copy_(torch.from_numpy(np.ascontiguousarray(cent)))
+        desc = {"workload": "video_chunk", "heads": H, "head_dim": D, "context": T, "q_len": Lq,
+                "keys": "256 centroids + int2 residual, groups of 32",
+                "values": "Walsh-Hadamard rotated, int2 per token, groups of 32",
+                "append_per_step": Lq}
+    elif name == "sensitivity":
+        d = synth.sensitivity_aware()
+        H, T, Lq = d["Hkv"], d["T"], d["Lq"]
+        cache = kv.KVCache(1, H, D, ((T + 63) // 64) * 64, key_mode=kv.KEY_CENTROID_QSAC,
+                           n_centroids=256, qsac_topk=4, psac_rank=8, value_mode=kv.VAL_HADAMARD)
+        K = synth.bf16_bits_to_f32(d["K"])[0]
+        cent = np.stack([K[d["kmeans_init"][0, h], h] for h in range(H)])[None]
+        cache.centroids.copy_(torch.from_numpy(np.ascontiguousarray(cent)))
+        qc = synth.bf16_bits_to_f32(d["q_cal"]).astype(np.float64)
+        w = (qc ** 2).mean(0).astype(np.float32)                       # [H][D]
+        U = np.stack([np.linalg.eigh(qc[:, h].T @ qc[:, h] / qc.shape[0])[1][:, ::-1][:, :8]
+                      for h in range(H)]).astype(np.float32)
+        cache.sens_w.copy_(torch.from_numpy(w[None]))
+        cache.psac_basis.copy_(torch.from_numpy(np.ascontiguousarray(U[None])))
+        desc = {"workload": "sensitivity", "heads": H, "head_dim": D, "context": T, "q_len": Lq,
+                "keys": "256 centroids, QSAC top-4, int2 residual, PSAC rank 8 fp16",
+                "values": "Walsh-Hadamard rotated, int2 per token, groups of 32",
+                "append_per_step": 0}
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    Kd, Vd, qd = to_dev(d["K"]), to_dev(d["V"]), to_dev(d["q"])
+    kv.kv_quantize_append(cache, Kd, Vd, 0)
+    Kn = to_dev(d["K_new"]) if "K_new" in d else None
+    Vn = to_dev(d["V_new"]) if "V_new" in d else None
+    out = torch.empty((1, Lq, H, D), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        kv.attn_int2_chunk(cache, T, qd, scale, out=out)
+        if ev:
+            ev[1].record()
+        if Kn is not None:
+            kv.kv_quantize_append(cache, Kn, Vn, T)
+        if ev:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_att = sum(e[0].elapsed_time(e[1]) for e in evs) / steps * 1e-3
+    t_app = sum(e[1].elapsed_time(e[2]) for e in evs) / steps * 1e-3
+    flops = 4.0 * Lq * T * D * H
+    tfs = flops / t_att / 1e12
+    rec = {"metric": "INT2 chunk-attn TFLOP/s & %MFMA peak", "value": round(tfs, 2),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+           "ms_per_step": round(wall / steps * 1e3, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
+           "config": desc,
+           "chunk_attention": {"us": round(t_att * 1e6, 1), "tflops": round(tfs, 2),
+                               "pct_mfma_peak": round(100 * tfs / MFMA_PEAK_TFS, 2),
+                               "flops": flops},
+           "roofline": {"kernel": "chunk_kernel", "bound": "mfma", "achieved": round(tfs, 2),
+                        "peak": MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                        "frac": round(tfs / MFMA_PEAK_TFS, 4), "traffic": None}}
+    if Kn is not None:
+        rec["quantize_append"] = {"us": round(t_app * 1e6, 1), "tokens": Lq,
+                                  "mtok_s": round(Lq / t_app / 1e6, 2)}
+    return rec
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="llm_decode",
+                    choices=["llm_decode", "long_history", "video_chunk", "sensitivity"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the path has no multi-GPU leg "
               "(sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
         return 2
+    if args.workload != "llm_decode":
+        import torch
+        torch.cuda.set_device(0)
+        print(json.dumps(chunk_workload(args.workload, args.steps, args.warmup)), flush=True)
+        return 0
 
     import numpy as np
     import torch

@@ -81,8 +81,11 @@ def calibrate(c: kv.KVCache, K_bits: np.ndarray, init: np.ndarray, iters: int,
     cent = np.zeros((L.batch, L.kv_heads, L.n_centroids, L.head_dim), np.float32)
     for b in range(L.batch):
         for h in range(L.kv_heads):
-            cent[b, h] = oracle.kmeans(np.ascontiguousarray(K[b, :, h]), L.n_centroids,
-                                       init[b, h], iters)[0]
+            if iters == 0:      # the initial picks themselves
+                cent[b, h] = K[b, init[b, h], h]
+            else:
+                cent[b, h] = oracle.kmeans(np.ascontiguousarray(K[b, :, h]), L.n_centroids,
+                                           init[b, h], iters)[0]
     c.centroids.copy_(torch.from_numpy(cent))
     if q_cal_bits is not None:
         qc = synth.bf16_bits_to_f32(q_cal_bits).astype(np.float64)   # [N][H][D]
