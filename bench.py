@@ -293,7 +293,7 @@ def main() -> int:
                             "effective_gbs": round(app_gbs, 1),
                             "pct_hbm_peak": round(100 * app_gbs / HBM_PEAK_GBS, 2),
                             "bytes": APPEND_BYTES},
-        "roofline": {"kernel": "window_append_kernel", "bound": "hbm",
+        "roofline": {"kernel": "tile_append_kernel", "bound": "hbm",
                      "achieved": round(app_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(app_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
         "roofline_decode": {"kernel": "decode_partial_kernel + decode_reduce_kernel",

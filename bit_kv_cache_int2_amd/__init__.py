@@ -112,7 +112,9 @@ class KVCache:
     [B,H,T/64,D] for window keys or [B,H,T,D/32] for centroid keys; k_tail
     i16 (bf16 bits) [B,H,64,D]; k_idx u8 [B,H,T]; centroids f32 [B,H,C,D];
     sens_w f32 [B,H,D]; psac_basis f32 [B,H,D,R]; k_psac i16 (fp16 bits)
-    [B,H,T,R]; v_codes u8 [B,H,T,D/4]; v_params i32 [B,H,T,D/32].
+    [B,H,T,R]; v_codes u8 [B,H,T/64,D,16] (per 64-token tile, channel-major:
+    token t of the tile, channel c in byte 16c + t/4, bits 2(t%4));
+    v_params i32 [B,H,T,D/32].
     Calibration inputs (centroids, sens_w, psac_basis) are filled by the caller.
     """
 
@@ -134,7 +136,7 @@ class KVCache:
             "sens_w": ((B, H, D), torch.float32),
             "psac_basis": ((B, H, D, max(psac_rank, 1)), torch.float32),
             "k_psac": ((B, H, T, max(psac_rank, 1)), torch.int16),
-            "v_codes": ((B, H, T, D // 4), torch.uint8),
+            "v_codes": ((B, H, T // WINDOW, D, 16), torch.uint8),
             "v_params": ((B, H, T, D // GROUP), torch.int32),
         }
         self.buffers = {}

@@ -144,9 +144,11 @@ __global__ __launch_bounds__(256) void chunk_kernel(const ChunkArgs a) {
     const int64_t rowbase = bh * a.Tcap + t0;
     __syncthreads();  // the previous tile's LDS tiles are consumed
     // ---- stage packed data (the tile lies inside the capacity)
+    // key rows [token][D/4]; the value tile is channel-major [D][16]
+    const int64_t vtile = (bh * (a.Tcap / 64) + tile) * (int64_t)D * 16;
     for (int e = tid; e < 64 * RB / 16; e += 256) {
       reinterpret_cast<uint4*>(kc)[e] = reinterpret_cast<const uint4*>(a.kcodes + rowbase * RB)[e];
-      reinterpret_cast<uint4*>(vc)[e] = reinterpret_cast<const uint4*>(a.vcodes + rowbase * RB)[e];
+      reinterpret_cast<uint4*>(vc)[e] = reinterpret_cast<const uint4*>(a.vcodes + vtile)[e];
     }
     for (int e = tid; e < 64 * NG; e += 256) vpw[e] = a.vparams[rowbase * NG + e];
     if (KM == 0) {
@@ -216,16 +218,21 @@ __global__ __launch_bounds__(256) void chunk_kernel(const ChunkArgs a) {
     // ---- dequantise values -> vt, transposed [dim][token]
     {
       _Float16 vv[4][TPT];
+      uint32_t cw[4];   // codes of tokens tg*TPT .. +TPT for channels 4bc .. 4bc+3
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint8_t* cr = &vc[(4 * bc + j) * 16 + (tg * TPT) / 4];
+        cw[j] = (TPT == 8) ? (uint32_t)*reinterpret_cast<const uint16_t*>(cr) : (uint32_t)*cr;
+      }
 #pragma unroll
       for (int u = 0; u < TPT; ++u) {
         const int t = tg * TPT + u;
         const bool ok = t0 + t < n;
-        const uint32_t byte = vc[t * RB + bc];
         const uint32_t pw = vpw[t * NG + (4 * bc) / kGroup];
         const float s = f16_bits_to_f32(pw), z = f16_bits_to_f32(pw >> 16);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          vv[j][u] = ok ? to_h(__builtin_fmaf((float)((byte >> (2 * j)) & 3u), s, z)) : (_Float16)0.0f;
+          vv[j][u] = ok ? to_h(__builtin_fmaf((float)((cw[j] >> (2 * u)) & 3u), s, z)) : (_Float16)0.0f;
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {

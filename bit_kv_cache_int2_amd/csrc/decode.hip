@@ -9,8 +9,9 @@
 //    bias + sum_c q~_c code_c over the raw 2-bit codes;
 //  * centroid keys: q . C_j is tabulated once per block, a logit is
 //    (q.C)[idx] + sum_g s_g (q_g . codes_g) + z_g sum(q_g) [+ (U^T q) . a];
-//  * values: p~ = p * s_(t,g) and the codes go through LDS, the z part is a
-//    per-lane running sum sum_t p_t z_(t,g).
+//  * values: p~ = p * s_(t,g) goes through LDS, each lane reads its channels'
+//    64-token code rows straight from the channel-major value tile, and the z
+//    part is a per-lane running sum sum_t p_t z_(t,g).
 // The online softmax works in base 2 (logits pre-scaled by log2 e) with
 // wave-shuffle maxima; each block merges its four waves and writes one
 // partial (o, m, l); a second kernel merges the splits, rotates rotated
@@ -50,14 +51,12 @@ template <int D, int G, int KM, int R>
 __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a) {
   constexpr int NG = D / kGroup;      // parameter groups per row
   constexpr int CPL = D / kWave;      // P.V channels per lane
-  constexpr int RW = D / 16;          // code dwords per token row
   __shared__ float qs[D][G];
   __shared__ float qc[KM == 1 ? G : 1][KM == 1 ? 256 : 1];
   __shared__ float qsum[G][NG];
   __shared__ float qp[G][R > 0 ? R : 1];
   __shared__ float qt[4][D][G];
   __shared__ float pt[4][kWave][NG][G];
-  __shared__ __align__(16) uint32_t vrow[4][kWave][RW];
   __shared__ float wm[4][G], wlv[4][G], wo[4][G][D];
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -238,22 +237,16 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
       m_run[g] = mn;
     }
 
-    // ---- values: p~ and codes through LDS
+    // ---- values: p~ through LDS; each lane reads its channels' tile rows
     {
       uint32_t vw[NG];
-      uint4 vr[D / 64];
       if (valid) {
         const int64_t tr = bh * a.Tcap + t;
 #pragma unroll
         for (int gr = 0; gr < NG; ++gr) vw[gr] = a.vparams[tr * NG + gr];
-        const uint4* row = reinterpret_cast<const uint4*>(a.vcodes + tr * (D / 4));
-#pragma unroll
-        for (int v = 0; v < D / 64; ++v) vr[v] = row[v];
       } else {
 #pragma unroll
         for (int gr = 0; gr < NG; ++gr) vw[gr] = 0u;
-#pragma unroll
-        for (int v = 0; v < D / 64; ++v) vr[v] = make_uint4(0u, 0u, 0u, 0u);
       }
 #pragma unroll
       for (int gr = 0; gr < NG; ++gr) {
@@ -265,20 +258,25 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
           pz[g][gr] = __builtin_fmaf(pg, zc, pz[g][gr]);
         }
       }
-#pragma unroll
-      for (int v = 0; v < D / 64; ++v) *reinterpret_cast<uint4*>(&vrow[wave][lane][4 * v]) = vr[v];
     }
     wave_lds_sync();
     {
-      // lane -> channels lane*CPL .. lane*CPL+CPL-1
+      // lane -> channels lane*CPL .. lane*CPL+CPL-1; a channel's 64 codes
+      // of this window are one 16-byte tile row (token tt at bits 2tt)
       const int c0 = lane * CPL;
       const int gr = c0 / kGroup;
-      const int dwi = c0 / 16, sh = 2 * (c0 % 16);
+      uint4 crow[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        crow[c] = *reinterpret_cast<const uint4*>(
+            a.vcodes + ((bh * (a.Tcap / kWindow) + win) * D + c0 + c) * 16);
       for (int tt = 0; tt < kWave; ++tt) {
-        const uint32_t dw = vrow[wave][tt][dwi];
         float cf[CPL];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) cf[c] = (float)((dw >> (sh + 2 * c)) & 3u);
+        for (int c = 0; c < CPL; ++c) {
+          const uint32_t wd = (tt < 16) ? crow[c].x : (tt < 32) ? crow[c].y : (tt < 48) ? crow[c].z : crow[c].w;
+          cf[c] = (float)((wd >> (2 * (tt & 15))) & 3u);
+        }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const float pg = pt[wave][tt][gr][g];

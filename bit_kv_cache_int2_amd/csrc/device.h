@@ -37,6 +37,15 @@ KVQ_DEV float f16_bits_to_f32(uint32_t b) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(b & 0xFFFFu));
 }
 
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// 16-byte load of data read exactly once (streamed inputs): non-temporal, so
+// it does not displace reusable lines from the caches.
+KVQ_DEV uint4 ld_stream(const void* p) {
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Unpack 8 bf16 held in a uint4 into fp32, canonicalising -0 to +0.
 KVQ_DEV void bf16x8_to_f32(const uint4 u, float* x) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};

@@ -1,15 +1,12 @@
 // Quantise-append into the packed INT2 cache, and centroid assignment.
 //
-//  * values ([OKV] rotated values, optional): one token row per D/8 lanes,
-//    8 channels (16 bytes of bf16) per lane, so a 32-channel parameter group
-//    is one lane quad and its min/max is two xor-shuffles.  The
-//    Walsh-Hadamard rotation runs in registers: three in-lane butterfly
-//    stages, then one xor-shuffle stage per remaining bit.
-//  * window keys ([OKV] per-window key ranges): one 256-thread block per
-//    (64-token window, sequence, head); the window is staged in LDS, each
-//    channel's min/max is a column scan, codes are packed row-wise and
-//    written as contiguous 8-byte pieces.  The block of the first window also
-//    writes the new tail after it has read the old one, so the two never race.
+//  * values ([OKV] rotated values, optional) and window keys ([OKV]
+//    per-window key ranges): one block per (head, 64-token tile, sequence),
+//    see tile_append_kernel.  A token row sits in D/8 lanes, 8 channels (16
+//    bytes of bf16) per lane, so a 32-channel parameter group is one lane
+//    quad and its min/max two xor-shuffles; the Walsh-Hadamard rotation runs
+//    in registers (three in-lane butterfly stages, then one xor-shuffle
+//    stage per remaining bit).
 //  * centroid keys ([QWM] 1): one lane per token keeps its key in registers
 //    and scans centroids staged 64 at a time in LDS (broadcast reads), in
 //    index order with the channel-order fp32 distance; QSAC keeps the best
@@ -56,142 +53,196 @@ KVQ_DEV void wht_row(float (&x)[8]) {
   for (int k = 0; k < 8; ++k) x[k] = x[k] * c + 0.0f;
 }
 
-// Quantise the 8-channel slice this lane holds of one token row (a row is
-// spread over D/8 consecutive lanes, so every lane of the row must take
-// part; `ok` false lanes only join the shuffles).
-template <int D, bool HAD>
-KVQ_DEV void value_slice(const uint16_t* src, bool ok, int j, uint8_t* code_row,
-                         uint32_t* prm_row) {
-  float x[8];
-  if (ok) {
-    bf16x8_to_f32(*reinterpret_cast<const uint4*>(src + j * 8), x);
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = 0.0f;
-  }
-  if (HAD) wht_row<D>(x);
-  float mn = x[0], mx = x[0];
-#pragma unroll
-  for (int k = 1; k < 8; ++k) {
-    mn = fminf(mn, x[k]);
-    mx = fmaxf(mx, x[k]);
-  }
-  mn = fminf(mn, __shfl_xor(mn, 1, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-  mn = fminf(mn, __shfl_xor(mn, 2, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-  const Q2 q = q2_make(mn, mx);
-  uint32_t bits = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) bits |= q2_code(x[k], q) << (2 * k);
-  if (ok) {
-    *reinterpret_cast<uint16_t*>(code_row + j * 2) = (uint16_t)bits;
-    if ((j & 3) == 0) prm_row[j >> 2] = q.word;
-  }
-}
-
-// Values only (centroid-key modes): rows (b, h, i) with i fastest.
-template <int D, bool HAD>
-__global__ __launch_bounds__(256) void quant_values_kernel(
-    const uint16_t* __restrict__ vin, uint8_t* __restrict__ vcodes,
-    uint32_t* __restrict__ vparams, int H, int Tcap, int cur_len, int n_new,
-    int64_t rows) {
-  constexpr int LPR = D / 8;
-  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
-  const int j = threadIdx.x & (LPR - 1);
-  const bool ok = row < rows;
-  const int64_t i = ok ? row % n_new : 0, bh = ok ? row / n_new : 0;
-  const int64_t h = bh % H, b = bh / H;
-  const int64_t orow = bh * Tcap + cur_len + i;
-  value_slice<D, HAD>(vin + ((b * n_new + i) * H + h) * D, ok, j, vcodes + orow * (D / 4),
-                      vparams + orow * (D / kGroup));
-}
-
-// ---------------------------------------------------------------- window keys
-// One block per (64-token window touched by the append, head, sequence):
-// the window's new value rows, then -- if the append completes the window --
-// its keys, quantised per channel over the 64 tokens (old tokens from the
-// tail, new ones from the input).  Block 0 also writes the tokens of the
-// window left unfinished into the tail, after its own reads of the old tail.
-template <int D, bool HAD>
-__global__ __launch_bounds__(256) void window_append_kernel(
+// ---------------------------------------------------------------- append
+// One block per (head, 64-token tile touched by the append, sequence).
+// Thread (r0, j) owns the 8-channel slice j of rows r0, r0 + RPP, ... of
+// the tile, for both keys and values, and issues all of its 16-byte loads
+// before any arithmetic.
+//  * values: quantised per row (lane quads); the codes are transposed into
+//    the tile's channel-major layout through LDS words (one 32-bit word holds
+//    16 tokens of one channel) and written back as whole tiles, keeping the
+//    codes of tokens an earlier append already stored in this tile;
+//  * keys (KEYS, window mode): when the append completes the window, each
+//    channel's min/max is reduced in registers (xor shuffles across the rows
+//    a wave holds, then one LDS exchange across the four waves), one thread
+//    per channel derives the thresholds, and every thread packs the codes of
+//    its own slices.  Block 0 also writes the tokens of the window left
+//    unfinished into the tail, after every thread has read the old tail.
+template <int D, bool HAD, bool KEYS>
+__global__ __launch_bounds__(256) void tile_append_kernel(
     const uint16_t* __restrict__ kin, const uint16_t* __restrict__ vin,
     uint8_t* __restrict__ kcodes, uint32_t* __restrict__ kparams,
     uint16_t* __restrict__ ktail, uint8_t* __restrict__ vcodes,
     uint32_t* __restrict__ vparams, int H, int Tcap, int cur_len, int n_new) {
-  constexpr int LPR = D / 8, RPP = 256 / LPR;  // lanes per row, rows per pass
-  constexpr int PARTS = 256 / D;              // threads per channel
-  constexpr int TPP = kWindow / PARTS;        // tokens per thread
-  __shared__ __align__(16) uint16_t tile[kWindow][D + 8];
-  __shared__ __align__(16) uint8_t codes[kWindow][D];
-  __shared__ float red_mn[PARTS][D], red_mx[PARTS][D];
+  constexpr int LPR = D / 8, RPP = 256 / LPR, NP = kWindow / RPP;
+  __shared__ float red_mn[4][D], red_mx[4][D];
+  __shared__ float thr[3][D];
+  __shared__ __align__(16) uint32_t vt[D][4];
 
-  const int job = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // heads vary fastest across blocks: the heads of one token are adjacent
+  // in the input, so concurrently running blocks read contiguous memory
+  const int h = blockIdx.x, job = blockIdx.y, b = blockIdx.z;
   const int64_t bh = (int64_t)b * H + h;
   const int end = cur_len + n_new;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = tid % LPR, r0 = tid / LPR;
   const int w = cur_len / kWindow + job;
-  const int t_lo = max(w * kWindow, cur_len), t_hi = min(w * kWindow + kWindow, end);
+  const int wb = w * kWindow;
+  const int t_lo = max(wb, cur_len), t_hi = min(wb + kWindow, end);
+  const bool full = KEYS && wb + kWindow <= end;
   const uint16_t* tail = ktail + bh * kWindow * D;
+  uint32_t* vtile = reinterpret_cast<uint32_t*>(vcodes + (bh * (Tcap / kWindow) + w) * (int64_t)D * 16);
 
-  for (int base = t_lo; base < t_hi; base += RPP) {
-    const int t = base + tid / LPR;
-    const bool ok = t < t_hi;
-    const int64_t orow = bh * Tcap + (ok ? t : t_lo);
-    value_slice<D, HAD>(vin + (((int64_t)b * n_new + (t - cur_len)) * H + h) * D, ok,
-                        tid % LPR, vcodes + orow * (D / 4), vparams + orow * (D / kGroup));
+  uint4 vraw[NP], kraw[NP];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const int p = wb + r0 + RPP * k;
+    const bool vok = p >= t_lo && p < t_hi;
+    vraw[k] = vok ? ld_stream(vin + (((int64_t)b * n_new + (p - cur_len)) * H + h) * D + j * 8)
+                  : make_uint4(0u, 0u, 0u, 0u);
+    if (full) {
+      const uint16_t* src = (p < cur_len) ? tail + (int64_t)(p & (kWindow - 1)) * D
+                                          : kin + (((int64_t)b * n_new + (p - cur_len)) * H + h) * D;
+      kraw[k] = ld_stream(src + j * 8);
+    }
   }
+  // value tile words.  A tile that starts fresh (no earlier tokens in it) is
+  // assembled from whole bytes; otherwise the words start from the codes of
+  // the tokens an earlier append stored and new codes are OR-ed in.
+  const int kept = t_lo - wb;   // tokens [wb, t_lo) are already in the tile
+  const bool fresh = (kept == 0) && (D == 128);
+  if (!fresh) {
+    for (int e = tid; e < D * 4; e += 256) {
+      const int wd = e & 3;
+      const int keep = min(max(kept - 16 * wd, 0), 16);      // tokens of this word to keep
+      const uint32_t mask = keep >= 16 ? 0xFFFFFFFFu : ((1u << (2 * keep)) - 1u);
+      vt[e >> 2][wd] = keep > 0 ? (vtile[e] & mask) : 0u;
+    }
+  }
+  __syncthreads();
 
-  if (w * kWindow + kWindow <= end) {
-    for (int e = tid; e < kWindow * D / 8; e += 256) {
-      const int t = e / (D / 8), jj = e % (D / 8);
-      const int p = w * kWindow + t;
-      const uint16_t* src =
-          (p < cur_len) ? tail + (int64_t)(p & (kWindow - 1)) * D
-                        : kin + (((int64_t)b * n_new + (p - cur_len)) * H + h) * D;
-      *reinterpret_cast<uint4*>(&tile[t][jj * 8]) = *reinterpret_cast<const uint4*>(src + jj * 8);
-    }
-    __syncthreads();
-    const int c = tid % D, part = tid / D;
-    float mn = bf16_to_f32(tile[part * TPP][c]) + 0.0f, mx = mn;
-    for (int t = part * TPP + 1; t < (part + 1) * TPP; ++t) {
-      const float x = bf16_to_f32(tile[t][c]) + 0.0f;
-      mn = fminf(mn, x);
-      mx = fmaxf(mx, x);
-    }
-    red_mn[part][c] = mn;
-    red_mx[part][c] = mx;
-    __syncthreads();
+  // ---- values
 #pragma unroll
-    for (int p2 = 0; p2 < PARTS; ++p2) {
-      mn = fminf(mn, red_mn[p2][c]);
-      mx = fmaxf(mx, red_mx[p2][c]);
+  for (int k = 0; k < NP; ++k) {
+    const int tt = r0 + RPP * k;                 // token within the tile
+    const int p = wb + tt;
+    const bool ok = p >= t_lo && p < t_hi;
+    float x[8];
+    bf16x8_to_f32(vraw[k], x);
+    if (HAD) wht_row<D>(x);
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) {
+      mn = fminf(mn, x[e]);
+      mx = fmaxf(mx, x[e]);
     }
+    mn = fminf(mn, __shfl_xor(mn, 1, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+    mn = fminf(mn, __shfl_xor(mn, 2, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
     const Q2 q = q2_make(mn, mx);
-    for (int t = part * TPP; t < (part + 1) * TPP; ++t)
-      codes[t][c] = (uint8_t)q2_code(bf16_to_f32(tile[t][c]) + 0.0f, q);
-    if (part == 0) kparams[(bh * (Tcap / kWindow) + w) * D + c] = q.word;
-    __syncthreads();
-    // pack: each thread emits 8 bytes (32 codes) of one token row
-    for (int e = tid; e < kWindow * (D / 32); e += 256) {
-      const int t = e / (D / 32), qd = e % (D / 32);
-      const uint4 c0 = *reinterpret_cast<const uint4*>(&codes[t][qd * 32]);
-      const uint4 c1 = *reinterpret_cast<const uint4*>(&codes[t][qd * 32 + 16]);
-      const uint32_t in[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-      uint32_t outw[2] = {0u, 0u};
+    uint32_t bits = 0;                       // channel 8j+e at bits [2e, 2e+1]
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        // four one-byte codes -> one packed byte
-        const uint32_t v = in[k];
-        const uint32_t byte = (v & 3u) | ((v >> 6) & 0xCu) | ((v >> 12) & 0x30u) | ((v >> 18) & 0xC0u);
-        outw[k >> 2] |= byte << (8 * (k & 3));
+    for (int e = 0; e < 8; ++e) bits |= q2_code(x[e], q) << (2 * e);
+    if (fresh) {
+      // D = 128: lanes 16i + j (i = 0..3) of this wave hold tokens 4*wave + i
+      // (+16k) of the same 8 channels.  Spread each lane's codes to one byte
+      // per channel (bits 2i), OR the four lanes together, and let lane i
+      // write the bytes of channels 8j + 2i, 8j + 2i + 1 (tokens 16k + 4w ..
+      // 16k + 4w + 3 form byte w of word (channel, k)).
+      const int i = lane >> 4;
+      auto spread = [](uint32_t t) {          // 4 two-bit codes -> bytes 0..3
+        t = (t | (t << 12)) & 0x000F000Fu;
+        return (t | (t << 6)) & 0x03030303u;
+      };
+      uint32_t v0 = spread(bits & 0xFFu) << (2 * i), v1 = spread(bits >> 8) << (2 * i);
+      v0 |= __shfl_xor(v0, 16, 64);
+      v1 |= __shfl_xor(v1, 16, 64);
+      v0 |= __shfl_xor(v0, 32, 64);
+      v1 |= __shfl_xor(v1, 32, 64);
+      uint8_t* vb = reinterpret_cast<uint8_t*>(&vt[0][0]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = 2 * i + u;
+        const uint32_t src = (e < 4) ? v0 : v1;
+        vb[((j * 8 + e) * 4 + (tt >> 4)) * 4 + wave] = (uint8_t)(src >> (8 * (e & 3)));
       }
-      *reinterpret_cast<uint2*>(kcodes + (bh * Tcap + (int64_t)w * kWindow + t) * (D / 4) + qd * 8) =
-          make_uint2(outw[0], outw[1]);
+    } else if (ok) {
+      const int sh = 2 * (tt & 15);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) atomicOr(&vt[j * 8 + e][tt >> 4], ((bits >> (2 * e)) & 3u) << sh);
+    }
+    if (ok && (j & 3) == 0) vparams[(bh * Tcap + p) * (D / kGroup) + (j >> 2)] = q.word;
+  }
+  __syncthreads();
+  for (int e = tid; e < D * 4 / 2; e += 256)
+    reinterpret_cast<uint2*>(vtile)[e] = reinterpret_cast<const uint2*>(&vt[0][0])[e];
+
+  if (!KEYS) return;
+  // ---- keys of a completed window
+  if (full) {
+    float kx[NP][8], mn[8], mx[8];
+#pragma unroll
+    for (int k = 0; k < NP; ++k) bf16x8_to_f32(kraw[k], kx[k]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      mn[e] = kx[0][e];
+      mx[e] = kx[0][e];
+#pragma unroll
+      for (int k = 1; k < NP; ++k) {
+        mn[e] = fminf(mn[e], kx[k][e]);
+        mx[e] = fmaxf(mx[e], kx[k][e]);
+      }
+      // rows held by this wave: lanes with the same j differ in bits >= log2(LPR)
+#pragma unroll
+      for (int o = LPR; o < 64; o <<= 1) {
+        mn[e] = fminf(mn[e], __shfl_xor(mn[e], o, 64));
+        mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], o, 64));
+      }
+    }
+    if (lane < LPR) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        red_mn[wave][j * 8 + e] = mn[e];
+        red_mx[wave][j * 8 + e] = mx[e];
+      }
+    }
+    __syncthreads();
+    if (tid < D) {
+      float a = red_mn[0][tid], c = red_mx[0][tid];
+#pragma unroll
+      for (int v = 1; v < 4; ++v) {
+        a = fminf(a, red_mn[v][tid]);
+        c = fmaxf(c, red_mx[v][tid]);
+      }
+      const Q2 q = q2_make(a, c);
+      thr[0][tid] = q.t0;
+      thr[1][tid] = q.t1;
+      thr[2][tid] = q.t2;
+      kparams[(bh * (Tcap / kWindow) + w) * D + tid] = q.word;
+    }
+    __syncthreads();
+    float t0[8], t1[8], t2[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      t0[e] = thr[0][j * 8 + e];
+      t1[e] = thr[1][j * 8 + e];
+      t2[e] = thr[2][j * 8 + e];
+    }
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      uint32_t bits = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = kx[k][e];
+        bits |= ((uint32_t)(x >= t0[e]) + (uint32_t)(x >= t1[e]) + (uint32_t)(x >= t2[e])) << (2 * e);
+      }
+      *reinterpret_cast<uint16_t*>(kcodes + (bh * Tcap + wb + r0 + RPP * k) * (D / 4) + j * 2) =
+          (uint16_t)bits;
     }
   }
   if (job == 0) {
-    __syncthreads();  // the first window has read the old tail
+    __syncthreads();  // every thread has read the old tail
     int ts = (end / kWindow) * kWindow;
     if (ts < cur_len) ts = cur_len;
     uint16_t* tw = ktail + bh * kWindow * D;
@@ -400,39 +451,21 @@ __global__ __launch_bounds__(256) void centroid_kernel(
   }
 }
 
-template <int D>
-hipError_t launch_values(const kvq_cache* c, const void* v, int cur_len, int n_new,
-                         hipStream_t st) {
-  const kvq_layout& L = c->layout;
-  const int64_t rows = (int64_t)L.batch * L.kv_heads * n_new;
-  const int64_t threads = rows * (D / 8);
-  const dim3 grid((unsigned)((threads + 255) / 256));
-  if (L.value_mode == KVQ_VAL_HADAMARD)
-    quant_values_kernel<D, true><<<grid, 256, 0, st>>>(
-        (const uint16_t*)v, (uint8_t*)c->v_codes, (uint32_t*)c->v_params, L.kv_heads,
-        L.capacity, cur_len, n_new, rows);
-  else
-    quant_values_kernel<D, false><<<grid, 256, 0, st>>>(
-        (const uint16_t*)v, (uint8_t*)c->v_codes, (uint32_t*)c->v_params, L.kv_heads,
-        L.capacity, cur_len, n_new, rows);
-  return hipGetLastError();
-}
-
-template <int D>
-hipError_t launch_window_append(const kvq_cache* c, const void* k, const void* v, int cur_len,
-                                int n_new, hipStream_t st) {
+template <int D, bool KEYS>
+hipError_t launch_tile_append(const kvq_cache* c, const void* k, const void* v, int cur_len,
+                              int n_new, hipStream_t st) {
   const kvq_layout& L = c->layout;
   const int end = cur_len + n_new;
   const int jobs = (end - 1) / kWindow - cur_len / kWindow + 1;
-  const dim3 grid((unsigned)jobs, (unsigned)L.kv_heads, (unsigned)L.batch);
+  const dim3 grid((unsigned)L.kv_heads, (unsigned)jobs, (unsigned)L.batch);
   auto args = [&](auto kern) {
     kern<<<grid, 256, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, (uint8_t*)c->k_codes,
                                (uint32_t*)c->k_params, (uint16_t*)c->k_tail,
                                (uint8_t*)c->v_codes, (uint32_t*)c->v_params, L.kv_heads,
                                L.capacity, cur_len, n_new);
   };
-  if (L.value_mode == KVQ_VAL_HADAMARD) args(window_append_kernel<D, true>);
-  else args(window_append_kernel<D, false>);
+  if (L.value_mode == KVQ_VAL_HADAMARD) args(tile_append_kernel<D, true, KEYS>);
+  else args(tile_append_kernel<D, false, KEYS>);
   return hipGetLastError();
 }
 
@@ -453,8 +486,8 @@ template <int D>
 hipError_t launch_append(const kvq_cache* c, const void* k, const void* v, int cur_len,
                          int n_new, hipStream_t st) {
   const kvq_layout& L = c->layout;
-  if (L.key_mode == KVQ_KEY_WINDOW) return launch_window_append<D>(c, k, v, cur_len, n_new, st);
-  hipError_t e = launch_values<D>(c, v, cur_len, n_new, st);
+  if (L.key_mode == KVQ_KEY_WINDOW) return launch_tile_append<D, true>(c, k, v, cur_len, n_new, st);
+  hipError_t e = launch_tile_append<D, false>(c, k, v, cur_len, n_new, st);
   if (e != hipSuccess) return e;
   const bool qsac = L.key_mode == KVQ_KEY_CENTROID_QSAC;
   if (L.psac_rank == 8)

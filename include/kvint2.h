@@ -33,8 +33,9 @@
  *    [x >= fma(1.5,s,z)] + [x >= fma(2.5,s,z)] (round half up to the
  *    nearest stored level), or 0 for every element when s == 0.
  *    Dequantised value: code * s + z.
- *  - Packing: 4 codes per byte, channel 4j+t of a token row in byte j,
- *    bits [2t, 2t+1] (codes 0,1,2,3 pack to 0xE4).
+ *  - Packing: 4 codes per byte, 2 bits each, lowest position in the lowest
+ *    bits (codes 0,1,2,3 pack to 0xE4): key codes by token row (channel 4j+t
+ *    in byte j), value codes by channel within 64-token tiles (see v_codes).
  *  - A parameter word is 32 bits: fp16 scale in the low half, fp16 zero in
  *    the high half.
  */
@@ -120,11 +121,17 @@ typedef struct kvq_layout {
  *   k_psac     u16 [B][H][Tcap][R]     fp16 PSAC coefficients
  *                                      a_m = fp16(sum_d fma(U_dm, e_d)),
  *                                      e = residual - dequantised residual
- *   v_codes    u8  [B][H][Tcap][D/4]
+ *   v_codes    u8  [B][H][Tcap/64][D][16]  value codes per 64-token tile,
+ *                                      channel-major: token t of the tile,
+ *                                      channel c in byte 16c + t/4, bits
+ *                                      [2(t%4), 2(t%4)+1] -- a channel's 64
+ *                                      codes are contiguous, as the
+ *                                      token-axis reduction of P.V reads them
  *   v_params   u32 [B][H][Tcap][D/32]
  * Buffers a mode does not use may be NULL.  Rows of tokens in an
  * unfinished window and tail slots at or beyond (length % 64) hold
- * unspecified bytes.  All buffers must be 16-byte aligned. */
+ * unspecified bytes (for values: the bits of tokens at or beyond the length in
+ * its 64-token tile).  All buffers must be 16-byte aligned. */
 typedef struct kvq_cache {
   kvq_layout layout;
   void* k_codes;

@@ -222,8 +222,8 @@ class Cache:
         z = np.zeros
         if self.k_codes is None:
             self.k_codes = z((B, H, T, D // 4), np.uint8)
-        if self.v_codes is None:
-            self.v_codes = z((B, H, T, D // 4), np.uint8)
+        if self.v_codes is None:      # per 64-token tile, channel-major
+            self.v_codes = z((B, H, T // WINDOW, D, 16), np.uint8)
         if self.v_params is None:
             self.v_params = z((B, H, T, D // GROUP), np.uint32)
         if self.k_params is None:

@@ -283,7 +283,10 @@ int orc_assign_qsac(const float* k, const float* cent, int C, int D,
 /* ------------------------------------------------------------------ */
 /* Cache update (the kv_quantize_append contract).                      */
 /* Buffers, per (b, h) with capacity Tcap tokens, D channels:           */
-/*   k_codes, v_codes  u8  [B][H][Tcap][D/4]                            */
+/*   k_codes           u8  [B][H][Tcap][D/4]   token rows (packing above)  */
+/*   v_codes           u8  [B][H][Tcap/64][D][16]  per 64-token tile,      */
+/*                     channel-major: the code of tile token t (0..63)     */
+/*                     for channel c sits in byte 16c + t/4, bits 2(t%4)   */
 /*   v_params          u32 [B][H][Tcap][D/32]                           */
 /*   k_params  window: u32 [B][H][Tcap/64][D]; centroid: u32 [..][Tcap][D/32] */
 /*   k_tail            u16 [B][H][64][D]    (bf16, window mode)          */
@@ -301,8 +304,14 @@ static size_t bh(const layout_t* L, int b, int h) {
   return (size_t)b * L->H + h;
 }
 
+/* Byte holding the value code of token p, channel c of sequence-head s. */
+static uint8_t* value_code_byte(uint8_t* v_codes, size_t s, int Tcap, int D, int p, int c) {
+  return v_codes + ((s * (size_t)(Tcap / WINDOW) + (size_t)(p / WINDOW)) * D + c) * 16 +
+         (p % WINDOW) / 4;
+}
+
 static void quantize_value_row(const layout_t* L, const uint16_t* v,
-                               uint8_t* code_row, uint32_t* prm) {
+                               uint8_t* v_codes, size_t s, int p, uint32_t* prm) {
   int D = L->D;
   float x[256];
   uint8_t codes[256];
@@ -313,7 +322,11 @@ static void quantize_value_row(const layout_t* L, const uint16_t* v,
     orc_q2(x + g * GROUP, GROUP, 1, codes + g * GROUP, &sh, &zh);
     prm[g] = pack_params(sh, zh);
   }
-  orc_pack_row(codes, D, code_row);
+  const int sh = 2 * (p % 4);
+  for (int c = 0; c < D; ++c) {
+    uint8_t* byte = value_code_byte(v_codes, s, L->Tcap, D, p, c);
+    *byte = (uint8_t)((*byte & ~(3u << sh)) | ((unsigned)codes[c] << sh));
+  }
 }
 
 static void quantize_centroid_key(const layout_t* L, const uint16_t* kin,
@@ -365,8 +378,7 @@ int orc_quantize_append(int B, int H, int D, int Tcap, int key_mode,
       for (int i = 0; i < n_new; ++i) {
         int p = cur_len + i;
         const uint16_t* v = v_in + (((size_t)b * n_new + i) * H + h) * D;
-        quantize_value_row(&L, v, v_codes + (s * Tcap + p) * rb,
-                           v_params + (s * Tcap + p) * ng);
+        quantize_value_row(&L, v, v_codes, s, p, v_params + (s * Tcap + p) * ng);
       }
       if (key_mode == KEY_WINDOW) {
         uint16_t* tail = k_tail + s * WINDOW * D;
@@ -460,10 +472,10 @@ void orc_dequant_values(int H, int D, int Tcap, const uint8_t* v_codes,
                         double* out) {
   size_t s = (size_t)b * H + h;
   for (int p = 0; p < n; ++p) {
-    const uint8_t* row = v_codes + (s * Tcap + p) * (D / 4);
-    for (int d = 0; d < D; ++d)
-      out[(size_t)p * D + d] =
-          deq(unpack_code(row, d), v_params[(s * Tcap + p) * (D / GROUP) + d / GROUP]);
+    for (int d = 0; d < D; ++d) {
+      const int code = (*value_code_byte((uint8_t*)v_codes, s, Tcap, D, p, d) >> (2 * (p % 4))) & 3;
+      out[(size_t)p * D + d] = deq(code, v_params[(s * Tcap + p) * (D / GROUP) + d / GROUP]);
+    }
   }
 }
 

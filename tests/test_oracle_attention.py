@@ -51,8 +51,11 @@ def test_attention_special_cases():
     out, lse = c.attention(np.zeros((1, 1, 1, 128)), 130, 0.1)
     assert np.allclose(out[0, 0, 0], c.values(0, 0, 130).mean(0), atol=1e-12)
     assert abs(lse[0, 0, 0] - math.log(130)) < 1e-12
-    # weights sum to one: identical value rows come back unchanged
-    c.v_codes[:] = c.v_codes[:, :, :1]
+    # weights sum to one: identical value rows come back unchanged (every
+    # token gets token 0's codes: value codes are stored per 64-token tile,
+    # channel-major, 2 bits per token)
+    first = c.v_codes[:, :, 0, :, 0] & 3                   # token 0, every channel
+    c.v_codes[:] = (first * 0x55).astype(np.uint8)[:, :, None, :, None]
     c.v_params[:] = c.v_params[:, :, :1]
     out, _ = c.attention(q, 130, 0.5)
     for i in range(3):
