@@ -296,7 +296,7 @@ def main() -> int:
         "roofline": {"kernel": "tile_append_kernel", "bound": "hbm",
                      "achieved": round(app_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(app_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
-        "roofline_decode": {"kernel": "decode_partial_kernel + decode_reduce_kernel",
+        "roofline_decode": {"kernel": "decode_mfma_kernel + decode_reduce_kernel",
                             "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4)},
     }

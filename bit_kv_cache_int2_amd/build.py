@@ -27,11 +27,17 @@ FLAGS = [
 
 SOURCES = ["api.cpp", "quantize.hip", "decode.hip", "chunk.hip"]
 
+# Per-source extras.  The decode kernel keeps its MFMA accumulators live
+# across a loop whose rare rescale branch scales them with VALU ops; with
+# accumulators in VGPRs the compiler no longer copies them between register
+# files on every iteration.
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

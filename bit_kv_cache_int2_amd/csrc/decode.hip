@@ -24,11 +24,20 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Most windows one split (one block) covers: eight per wave.
+constexpr int kDecodeMaxWindows = 32;
+// Fourth word of a raw buffer resource (32-bit data format), and the
+// non-temporal cache policy for streamed cache reads.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kNT = 2;
 
+// Orders one wave's LDS writes before its following LDS reads (data shared
+// between lanes of a wave).  The fences are restricted to LDS ("local"), so
+// they do not wait for the wave's outstanding global loads.
 KVQ_DEV void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
 struct DecodeArgs {
@@ -326,6 +335,412 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
   }
 }
 
+// ---------------------------------------------------------------- MFMA decode
+// Window keys, head_dim 128, 4 query heads per kv head.  Both products run
+// on v_mfma_f32_16x16x32_f16 with the 2-bit codes as one operand, encoded
+// as exact fp16 values base + code: a code moved to mantissa bits 8-9 under
+// exponent 2 reads 4 + code, bits 6-7 under exponent 4 read 16 + code,
+// bits 4-5 under exponent 6 read 64 + code.  Code i of a 32-bit code word
+// sits at bit 2i of its 16-bit half: shifts by 6, 0 and -6 bring codes
+// (0, 1), (2, 3, 4) and (5, 6, 7) to those positions, and one and-or per
+// operand dword places codes (i, i + 8), so a 16-code word costs two
+// shifts and eight and-ors.  Position i has base {16, 4, 64, 16, 4, 64, 16,
+// 4}[i].  All products are exact.
+//   S^T[token][head] = sum_c (base_c + code[token][c]) qt[head][c] with the
+//     hi and lo fp16 parts of qt = q * s_w * scale * log2 e stacked along K
+//     (the same code operand multiplies both); the window bias
+//     sum_c q_c (z_c - base_c s_c), the accumulator's initial value, adds
+//     the zero points and removes the base term;
+//   O^T[c][col] = sum_t (base_t + code[t][c]) pt[t][col] with col = 4 group
+//     + head and pt = fp16(p * s_(t,group)); only the columns of a channel's
+//     own group are kept; the base term comes from one more MFMA against a
+//     constant operand holding the bases (same fp16 pt values), and
+//     sum_t p z_(t,group) is a per-lane fp32 sum.
+// B columns 4..15 of S^T hold copies of columns 0..3, so every lane's
+// accumulator holds logits of head (lane % 4).  A wave owns at most eight
+// windows of its split (every fourth one).  Pass 1 streams their key codes,
+// stores the logits (base 2) in LDS and takes the exact per-head maximum;
+// the partial window (bf16 key tail) of a sequence is scored with fp32 dot
+// products.  Pass 2 streams the value codes and accumulates p = 2^(l - m)
+// <= 1: no running rescale.  Each pass loads window w + 4 while it
+// computes window w.
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// (t & mask) | bits.  gfx9 VOP3 encodings take no literal constants and at
+// most one scalar operand, so v_and_or_b32 needs one of the constants in a
+// VGPR: the bits arrive through an empty asm statement, which hides their
+// value and makes the compiler keep them in a register.
+KVQ_DEV uint32_t and_or(uint32_t t, uint32_t mask, uint32_t bits) { return (t & mask) | bits; }
+
+// Operand dwords for the 16 codes of word d: out[i] holds codes (i, i + 8)
+// in its (low, high) half as base_i + code.  No bit of one half reaches the
+// selected bits of the other: a left shift by 6 moves the low half to bits
+// 6..21 (the high half's codes sit at 22 and up), a right shift by 6 moves
+// the high half to bits 10..25 (the low half's codes end at bit 9).
+struct CodeOr {
+  uint32_t b64, b16, b4;   // exponent bits of 64, 16 and 4 in both halves
+};
+KVQ_DEV void code_word(uint32_t d, const CodeOr& k, uint32_t out[8]) {
+  const uint32_t l6 = d << 6, r6 = d >> 6;
+  out[0] = and_or(l6, 0x00C000C0u, k.b16);
+  out[1] = and_or(l6, 0x03000300u, k.b4);
+  out[2] = and_or(d, 0x00300030u, k.b64);
+  out[3] = and_or(d, 0x00C000C0u, k.b16);
+  out[4] = and_or(d, 0x03000300u, k.b4);
+  out[5] = and_or(r6, 0x00300030u, k.b64);
+  out[6] = and_or(r6, 0x00C000C0u, k.b16);
+  out[7] = and_or(r6, 0x03000300u, k.b4);
+}
+
+// Base of code-word position i.
+KVQ_DEV float code_base(int i) {
+  return (i == 2 || i == 5) ? 64.0f : ((i == 1 || i == 4 || i == 7) ? 4.0f : 16.0f);
+}
+
+KVQ_DEV h8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(h8, make_uint4(a, b, c, d));
+}
+
+// Sums four per-lane values over the wave: afterwards every lane of row r
+// (lanes 16r .. 16r + 15) holds the total of v[r].  Each xor exchange
+// halves the values a lane keeps (lanes below 32 keep v[0], v[1]; then rows
+// with bit 4 clear keep the first of the two), then rotations inside each
+// row finish the sum.  (The permlane swap builtins would save two
+// exchanges, but this compiler merges their two results when both feed
+// one expression.)
+KVQ_DEV float wave_sum4(const float v[4]) {
+  const int lane = threadIdx.x & 63;
+  const bool hi32 = (lane & 32) != 0, hi16 = (lane & 16) != 0;
+  const float k0 = hi32 ? v[2] : v[0], k1 = hi32 ? v[3] : v[1];
+  const float s0 = hi32 ? v[0] : v[2], s1 = hi32 ? v[1] : v[3];
+  const float a0 = k0 + __shfl_xor(s0, 32, 64), a1 = k1 + __shfl_xor(s1, 32, 64);
+  const float k = hi16 ? a1 : a0, sn = hi16 ? a0 : a1;
+  float y = k + __shfl_xor(sn, 16, 64);
+  y += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), 0x128, 0xF, 0xF, false));
+  y += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), 0x124, 0xF, 0xF, false));
+  y += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), 0x122, 0xF, 0xF, false));
+  y += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), 0x121, 0xF, 0xF, false));
+  return y;
+}
+
+__global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
+  constexpr int D = 128, G = 4, MAXW = kDecodeMaxWindows / 4;
+  __shared__ float qs[D][G];                                   // q * scale * log2 e
+  __shared__ __align__(16) uint32_t qb[4][4][2][4][4][4];      // [wave][head][hi,lo][g][ks] 8 halfs
+  __shared__ __align__(16) float sl[4][MAXW][G][kWave];        // [wave][slot][head][token] logits
+  __shared__ __align__(16) _Float16 pb[4][16][4][2][8];        // [wave][col][g][kk] 8 halfs
+  __shared__ float wm[4][G], wlv[4][G], wo[4][G][D];
+
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // the wave index is uniform in a wave; saying so keeps window offsets scalar
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int hq0 = h * G;
+  for (int e = tid; e < G * D; e += 256) {
+    const int hh = e / D, c = e % D;
+    const int64_t qi = ((int64_t)b * a.Hq + hq0 + hh) * D + c;
+    const float qv = a.q_bf16 ? bf16_to_f32(((const uint16_t*)a.q)[qi]) : ((const float*)a.q)[qi];
+    qs[c][hh] = qv * a.scale_log2;
+  }
+  __syncthreads();
+
+  const int t_begin = s * a.split_len;
+  const int t_end = min(t_begin + a.split_len, a.n_tokens);
+  const int n_full_win = a.n_tokens / kWindow;
+  const int w_end = (t_end + kWindow - 1) / kWindow;
+  const int wf_end = min(w_end, n_full_win);
+  const int w_first = t_begin / kWindow + wave;               // this wave's first window
+
+  CodeOr kor = {0x54005400u, 0x4C004C00u, 0x44004400u};
+  asm volatile("" : "+v"(kor.b64), "+v"(kor.b16), "+v"(kor.b4));
+  // buffer views of this (sequence, kv head): window offsets go in the
+  // scalar offset, per-lane offsets are fixed; lanes past the end read 0
+  const int nwin_cap = a.Tcap / kWindow;
+  const auto rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.kcodes + bh * a.Tcap * (D / 4)), (short)0, a.Tcap * (D / 4), kBufferWord3);
+  const auto rkp = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.kparams + bh * nwin_cap * D), (short)0, nwin_cap * D * 4, kBufferWord3);
+  const auto rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.vcodes + bh * nwin_cap * (int64_t)D * 16), (short)0, nwin_cap * D * 16, kBufferWord3);
+  const auto rvp = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.vparams + bh * a.Tcap * 4), (short)0, a.n_tokens * 16, kBufferWord3);
+
+  // ================= pass 1: logits
+  // this lane's channel pair for the query fold: ca and ca + 8, position
+  // fi of its code word (even: base 16, odd: base 4)
+  const int fi = lane & 7;
+  const int ca = (lane >> 3) * 16 + fi, cb = ca + 8;
+  const int qks = 2 * ((lane >> 3) & 1) + (fi >> 2), qi2 = fi & 3, qg = lane >> 4;
+  const float fbase = code_base(fi);
+  float qa[G], qbv[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    qa[hh] = qs[ca][hh];
+    qbv[hh] = qs[cb][hh];
+  }
+  struct KWin {
+    uint2 kc[4];       // key codes: token ts*16 + c16, channels 32g .. 32g+31
+    uint32_t pa, pb;   // window parameters of channels ca, cb
+  };
+  const int ko = c16 * (D / 4) + 8 * g, vo = c16 * 16 + 4 * g;
+  auto fetch_keys = [&](int win, KWin& f) {
+    const int w = __builtin_amdgcn_readfirstlane(win);
+    const int so = w * kWindow * (D / 4), sp = w * D * 4;
+#pragma unroll
+    for (int ts = 0; ts < 4; ++ts) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rk, ko + ts * 16 * (D / 4), so, kNT);
+      f.kc[ts] = make_uint2(v[0], v[1]);
+    }
+    f.pa = __builtin_amdgcn_raw_buffer_load_b32(rkp, ca * 4, sp, kNT);
+    f.pb = __builtin_amdgcn_raw_buffer_load_b32(rkp, cb * 4, sp, kNT);
+  };
+  struct VWin {
+    uint32_t vcw[8];   // value codes: channel mt*16 + c16, tokens 16g .. 16g+15
+    uint4 vp;          // value parameters of token lane
+  };
+  auto fetch_values = [&](int win, VWin& f) {
+    const int w = __builtin_amdgcn_readfirstlane(win);
+    const int so = w * D * 16;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+      f.vcw[mt] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo + mt * 256, so, kNT);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rvp, lane * 16, w * kWindow * 16, kNT);
+    f.vp = make_uint4(v[0], v[1], v[2], v[3]);
+  };
+
+  float mx = -__builtin_inff();        // running max of head (lane % 4)
+  auto window_logits = [&](const KWin& cur, int slot) {
+    // fold the query into the window: qt hi/lo -> LDS, bias
+    const float sa = f16_bits_to_f32(cur.pa), za = f16_bits_to_f32(cur.pa >> 16);
+    const float sb = f16_bits_to_f32(cur.pb), zb = f16_bits_to_f32(cur.pb >> 16);
+    const float zca = __builtin_fmaf(-fbase, sa, za), zcb = __builtin_fmaf(-fbase, sb, zb);
+    float bias[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const auto hi = __builtin_amdgcn_cvt_pkrtz(qa[hh] * sa, qbv[hh] * sb);
+      const float la = __builtin_fmaf(qa[hh], sa, -(float)hi[0]);
+      const float lb = __builtin_fmaf(qbv[hh], sb, -(float)hi[1]);
+      const auto lo = __builtin_amdgcn_cvt_pkrtz(la, lb);
+      qb[wave][hh][0][qg][qks][qi2] = __builtin_bit_cast(uint32_t, hi);
+      qb[wave][hh][1][qg][qks][qi2] = __builtin_bit_cast(uint32_t, lo);
+      bias[hh] = __builtin_fmaf(qa[hh], zca, qbv[hh] * zcb);
+    }
+    // row r of bsum holds the bias of head r; this lane's head is c16 % 4
+    const float bsum = wave_sum4(bias);
+    const float bl = __shfl(bsum, (c16 & 3) * 16, 64);
+    const f4 binit = f4{bl, bl, bl, bl};
+    wave_lds_sync();
+    h8 bq[4][2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt)
+        bq[ks][pt] = *reinterpret_cast<const h8*>(&qb[wave][c16 & 3][pt][g][ks][0]);
+    // four independent accumulator chains (token slabs ts), step-major
+    f4 sacc[4] = {binit, binit, binit, binit};
+#pragma unroll
+    for (int wd = 0; wd < 2; ++wd) {
+      uint32_t kw[4][8];
+#pragma unroll
+      for (int ts = 0; ts < 4; ++ts) code_word(wd ? cur.kc[ts].y : cur.kc[ts].x, kor, kw[ts]);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+          for (int ts = 0; ts < 4; ++ts)
+            sacc[ts] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                as_h8(kw[ts][4 * hf], kw[ts][4 * hf + 1], kw[ts][4 * hf + 2], kw[ts][4 * hf + 3]),
+                bq[2 * wd + hf][pt], sacc[ts], 0, 0, 0);
+    }
+#pragma unroll
+    for (int ts = 0; ts < 4; ++ts) {
+      mx = fmaxf(fmaxf(fmaxf(mx, sacc[ts][0]), sacc[ts][1]), fmaxf(sacc[ts][2], sacc[ts][3]));
+      if (c16 < 4) *reinterpret_cast<f4*>(&sl[wave][slot][c16][ts * 16 + 4 * g]) = sacc[ts];
+    }
+  };
+
+  VWin va, vb;
+  if (w_first < w_end) fetch_values(w_first, va);            // first window of pass 2
+  int nslot = 0;
+  {
+    KWin ka, kb;
+    int win = w_first;
+    if (win < wf_end) fetch_keys(win, ka);
+    while (win < wf_end) {
+      if (win + 4 < wf_end) fetch_keys(win + 4, kb);
+      window_logits(ka, nslot++);
+      win += 4;
+      if (win >= wf_end) break;
+      if (win + 4 < wf_end) fetch_keys(win + 4, ka);
+      window_logits(kb, nslot++);
+      win += 4;
+    }
+  }
+  // lanes with equal (lane % 4) hold the same head: reduce within rows by
+  // rotations of 4 and 8, then across the four rows
+  mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, mx), 0x124, 0xF, 0xF, false)));
+  mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, mx), 0x128, 0xF, 0xF, false)));
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  float M[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+    M[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), hh));
+  // the unfinished window: bf16 keys from the tail, plain fp32 dot products
+  const int wt = w_first + 4 * nslot;
+  if (wt == n_full_win && wt < w_end) {
+    const int t = wt * kWindow + lane;
+    float lg[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) lg[hh] = -__builtin_inff();
+    if (t < t_end) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) lg[hh] = 0.0f;
+      const uint16_t* kt = a.ktail + (bh * kWindow + lane) * D;
+#pragma unroll 4
+      for (int v = 0; v < D / 8; ++v) {
+        float x[8];
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(kt + v * 8), x);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) lg[hh] = __builtin_fmaf(qs[v * 8 + u][hh], x[u], lg[hh]);
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      sl[wave][nslot][hh][lane] = lg[hh];
+      M[hh] = fmaxf(M[hh], wave_max(lg[hh]));
+    }
+    ++nslot;
+  }
+  wave_lds_sync();
+
+  // ================= pass 2: p = 2^(l - M), P.V
+  float l_lane[G], pz[G][4];
+  f4 o[8], ocorr;
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    l_lane[hh] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pz[hh][q] = 0.0f;
+  }
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) o[mt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  ocorr = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  // bases of the value operand: dword j of k-step k2 holds the tokens of
+  // code-word positions i = 4 k2 + j and i + 8
+  h8 vbase[2];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vbase[k2][j] = (_Float16)code_base(4 * k2 + j / 2);
+  // P~ -> LDS in the operand's token order: token 16 gk + o pairs with
+  // o + 8; k index 2 i' + (o >= 8) of k-step (o % 8) / 4
+  const int kk = (c16 & 7) >> 2, jj = 2 * (c16 & 3) + (c16 >> 3);
+  auto window_pv = [&](const VWin& cur, int slot) {
+    const uint32_t vw[4] = {cur.vp.x, cur.vp.y, cur.vp.z, cur.vp.w};
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float p = __builtin_amdgcn_exp2f(sl[wave][slot][hh][lane] - M[hh]);
+      l_lane[hh] += p;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float sc = f16_bits_to_f32(vw[q]), zc = f16_bits_to_f32(vw[q] >> 16);
+        pz[hh][q] = __builtin_fmaf(p, zc, pz[hh][q]);
+        pb[wave][4 * q + hh][g][kk][jj] = (_Float16)(p * sc);
+      }
+    }
+    wave_lds_sync();
+    h8 bpv[2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) bpv[k2] = *reinterpret_cast<const h8*>(&pb[wave][c16][g][k2][0]);
+#pragma unroll
+    for (int m0 = 0; m0 < 8; m0 += 4) {
+      uint32_t vx[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) code_word(cur.vcw[m0 + u], kor, vx[u]);
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          o[m0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              as_h8(vx[u][4 * k2], vx[u][4 * k2 + 1], vx[u][4 * k2 + 2], vx[u][4 * k2 + 3]), bpv[k2],
+              o[m0 + u], 0, 0, 0);
+    }
+    ocorr = __builtin_amdgcn_mfma_f32_16x16x32_f16(vbase[0], bpv[0], ocorr, 0, 0, 0);
+    ocorr = __builtin_amdgcn_mfma_f32_16x16x32_f16(vbase[1], bpv[1], ocorr, 0, 0, 0);
+    wave_lds_sync();
+  };
+  {
+    int slot = 0, win = w_first;
+    while (slot < nslot) {
+      if (slot + 1 < nslot) fetch_values(win + 4, vb);
+      window_pv(va, slot);
+      ++slot;
+      win += 4;
+      if (slot >= nslot) break;
+      if (slot + 1 < nslot) fetch_values(win + 4, va);
+      window_pv(vb, slot);
+      ++slot;
+      win += 4;
+    }
+  }
+  float m_ref[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) m_ref[hh] = nslot > 0 ? M[hh] : -__builtin_inff();
+
+  // ---- wave partial: lane (col n = 4 q + head, g) keeps channels of group q
+  {
+    const int hh = c16 & 3, q = c16 >> 2;
+    float lsum[G], zs[G][4];
+#pragma unroll
+    for (int x = 0; x < G; ++x) {
+      lsum[x] = wave_sum(l_lane[x]);
+#pragma unroll
+      for (int y = 0; y < 4; ++y) zs[x][y] = wave_sum(pz[x][y]);
+    }
+    float zq = 0.0f;
+#pragma unroll
+    for (int x = 0; x < G; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+        if (x == hh && y == q) zq = zs[x][y];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      if ((mt >> 1) == q) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wo[wave][hh][mt * 16 + 4 * g + i] = o[mt][i] - ocorr[i] + zq;
+      }
+    }
+    if (lane < G) {
+      wm[wave][lane] = m_ref[lane];
+      wlv[wave][lane] = lsum[lane];
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < G * (D + 2); e += 256) {
+    const int hh = e / (D + 2), c = e % (D + 2);
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][hh]);
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = (wm[w][hh] == -__builtin_inff()) ? 0.0f : exp2f(wm[w][hh] - M);
+      const float v = (c < D) ? wo[w][hh][c] : wlv[w][hh];
+      acc = __builtin_fmaf(f, v, acc);
+    }
+    float* dst = a.ws + (((int64_t)s * gridDim.z + b) * a.Hq + hq0 + hh) * (D + 2);
+    if (c < D) dst[c] = acc;
+    else if (c == D) dst[D] = M;
+    else dst[D + 1] = acc;
+  }
+}
+
 template <int D, bool HAD>
 __global__ __launch_bounds__(128) void decode_reduce_kernel(const float* __restrict__ ws, int S,
                                                             int BHq, void* out, int out_bf16,
@@ -386,6 +801,11 @@ hipError_t launch_partial_mode(const DecodeArgs& a, int key_mode, int R, int B, 
 template <int D>
 hipError_t launch_partial_g(const DecodeArgs& a, int G, int key_mode, int R, int B,
                             hipStream_t st) {
+  if (D == 128 && G == 4 && key_mode == KVQ_KEY_WINDOW) {
+    const dim3 grid((unsigned)a.S, (unsigned)a.H, (unsigned)B);
+    decode_mfma_kernel<<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
+  }
   switch (G) {
     case 1: return launch_partial_mode<D, 1>(a, key_mode, R, B, st);
     case 2: return launch_partial_mode<D, 2>(a, key_mode, R, B, st);
@@ -402,6 +822,8 @@ int decode_splits(const kvq_layout* L, int q_heads, int n_tokens) {
   const int units = L->batch * L->kv_heads;
   int S = (2048 + units - 1) / units;
   if (S > n_win) S = n_win;
+  const int s_min = (n_win + kDecodeMaxWindows - 1) / kDecodeMaxWindows;
+  if (S < s_min) S = s_min;
   if (S < 1) S = 1;
   const int per = (n_win + S - 1) / S;
   return (n_win + per - 1) / per;
