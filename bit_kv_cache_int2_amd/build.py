@@ -27,11 +27,11 @@ FLAGS = [
 
 SOURCES = ["api.cpp", "quantize.hip", "decode.hip", "chunk.hip"]
 
-# Per-source extras.  The decode kernel keeps its MFMA accumulators live
-# across a loop whose rare rescale branch scales them with VALU ops; with
-# accumulators in VGPRs the compiler no longer copies them between register
-# files on every iteration.
-EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extras for the decode kernels: MFMA accumulators in VGPRs (no
+# copies between register files), and no NaN operands (attention never
+# produces one from finite cache contents), which lets max chains compile
+# to v_max3_f32 without quieting each MFMA result first.
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

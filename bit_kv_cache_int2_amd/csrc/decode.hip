@@ -16,6 +16,8 @@
 // wave-shuffle maxima; each block merges its four waves and writes one
 // partial (o, m, l); a second kernel merges the splits, rotates rotated
 // values back and writes out/lse.
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -30,6 +32,8 @@ constexpr int kDecodeMaxWindows = 32;
 // non-temporal cache policy for streamed cache reads.
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kNT = 2;
+// Prefetch distances (windows) of the MFMA decode's key and value streams.
+constexpr int kKeyAhead = 3, kValAhead = 3;
 
 // Orders one wave's LDS writes before its following LDS reads (data shared
 // between lanes of a wave).  The fences are restricted to LDS ("local"), so
@@ -424,12 +428,55 @@ KVQ_DEV float wave_sum4(const float v[4]) {
   return y;
 }
 
+// Value of lane + 4 inside the 16-lane row (0 past its end).
+KVQ_DEV float row_shl4(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x104, 0xF, 0xF, false));
+}
+
+// Sums sixteen per-lane values over the wave and returns, in each lane, the
+// total of v[j] for j = jsel (0..15).  Four exchanges halve the values a lane
+// keeps (partners across bits 5, 4, 3 and 2 of the lane: xor 32, xor 16,
+// a rotation by 8 inside the row, a mirror inside each half row), so lane
+// l ends with a partial of v[(l >> 2) & 15]; a quad sum completes it and
+// one shuffle fetches the wanted total.
+KVQ_DEV float wave_sum16_at(const float v[16], int jsel) {
+  const int lane = threadIdx.x & 63;
+  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8, b2 = lane & 4;
+  float a[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const float keep = b5 ? v[m + 8] : v[m], send = b5 ? v[m] : v[m + 8];
+    a[m] = keep + __shfl_xor(send, 32, 64);
+  }
+  float c4[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const float keep = b4 ? a[n + 4] : a[n], send = b4 ? a[n] : a[n + 4];
+    c4[n] = keep + __shfl_xor(send, 16, 64);
+  }
+  float c2[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const float keep = b3 ? c4[r + 2] : c4[r], send = b3 ? c4[r] : c4[r + 2];
+    c2[r] = keep + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                       0, __builtin_bit_cast(int, send), 0x128, 0xF, 0xF, false));   // row_ror:8
+  }
+  const float keep = b2 ? c2[1] : c2[0], send = b2 ? c2[0] : c2[1];
+  float y = keep + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                       0, __builtin_bit_cast(int, send), 0x141, 0xF, 0xF, false));   // row_half_mirror
+  y += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  y += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  return __shfl(y, 4 * jsel, 64);
+}
+
 __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
   constexpr int D = 128, G = 4, MAXW = kDecodeMaxWindows / 4;
   __shared__ float qs[D][G];                                   // q * scale * log2 e
-  __shared__ __align__(16) uint32_t qb[4][4][2][4][4][4];      // [wave][head][hi,lo][g][ks] 8 halfs
-  __shared__ __align__(16) float sl[4][MAXW][G][kWave];        // [wave][slot][head][token] logits
-  __shared__ __align__(16) _Float16 pb[4][16][4][2][8];        // [wave][col][g][kk] 8 halfs
+  // LDS strides are padded so that a wave's accesses spread over the 64
+  // banks: qb heads by 4 dwords, sl heads by 16, pb columns by 4
+  __shared__ __align__(16) uint32_t qb[4][4][132];             // [wave][head][(hi,lo) g ks] 8 halfs
+  __shared__ __align__(16) float sl[4][MAXW][G][kWave + 16];   // [wave][slot][head][token] logits
+  __shared__ __align__(16) _Float16 pb[4][16][72];             // [wave][col][(g kk) 8 halfs]
   __shared__ float wm[4][G], wlv[4][G], wo[4][G][D];
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -495,6 +542,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
     }
     f.pa = __builtin_amdgcn_raw_buffer_load_b32(rkp, ca * 4, sp, kNT);
     f.pb = __builtin_amdgcn_raw_buffer_load_b32(rkp, cb * 4, sp, kNT);
+    // keep each window's loads together and in issue order: the wait for
+    // window w then leaves every later window's loads in flight
+    __builtin_amdgcn_sched_barrier(0);
   };
   struct VWin {
     uint32_t vcw[8];   // value codes: channel mt*16 + c16, tokens 16g .. 16g+15
@@ -508,6 +558,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
       f.vcw[mt] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo + mt * 256, so, kNT);
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(rvp, lane * 16, w * kWindow * 16, kNT);
     f.vp = make_uint4(v[0], v[1], v[2], v[3]);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   float mx = -__builtin_inff();        // running max of head (lane % 4)
@@ -523,21 +574,23 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
       const float la = __builtin_fmaf(qa[hh], sa, -(float)hi[0]);
       const float lb = __builtin_fmaf(qbv[hh], sb, -(float)hi[1]);
       const auto lo = __builtin_amdgcn_cvt_pkrtz(la, lb);
-      qb[wave][hh][0][qg][qks][qi2] = __builtin_bit_cast(uint32_t, hi);
-      qb[wave][hh][1][qg][qks][qi2] = __builtin_bit_cast(uint32_t, lo);
+      qb[wave][hh][qg * 16 + qks * 4 + qi2] = __builtin_bit_cast(uint32_t, hi);
+      qb[wave][hh][64 + qg * 16 + qks * 4 + qi2] = __builtin_bit_cast(uint32_t, lo);
       bias[hh] = __builtin_fmaf(qa[hh], zca, qbv[hh] * zcb);
     }
-    // row r of bsum holds the bias of head r; this lane's head is c16 % 4
+    // row r of bsum holds the bias of head r; it enters the hi columns
+    // (0..3) of the accumulator only
     const float bsum = wave_sum4(bias);
     const float bl = __shfl(bsum, (c16 & 3) * 16, 64);
-    const f4 binit = f4{bl, bl, bl, bl};
+    const float bc = c16 < 4 ? bl : 0.0f;
+    const f4 binit = f4{bc, bc, bc, bc};
     wave_lds_sync();
-    h8 bq[4][2];
+    // B operand columns: 0..3 hi parts of heads 0..3, 4..7 lo parts,
+    // 8..15 copies (never read)
+    h8 bq[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int pt = 0; pt < 2; ++pt)
-        bq[ks][pt] = *reinterpret_cast<const h8*>(&qb[wave][c16 & 3][pt][g][ks][0]);
+      bq[ks] = *reinterpret_cast<const h8*>(&qb[wave][c16 & 3][((c16 >> 2) & 1) * 64 + g * 16 + ks * 4]);
     // four independent accumulator chains (token slabs ts), step-major
     f4 sacc[4] = {binit, binit, binit, binit};
 #pragma unroll
@@ -548,89 +601,35 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-          for (int ts = 0; ts < 4; ++ts)
-            sacc[ts] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                as_h8(kw[ts][4 * hf], kw[ts][4 * hf + 1], kw[ts][4 * hf + 2], kw[ts][4 * hf + 3]),
-                bq[2 * wd + hf][pt], sacc[ts], 0, 0, 0);
+        for (int ts = 0; ts < 4; ++ts)
+          sacc[ts] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              as_h8(kw[ts][4 * hf], kw[ts][4 * hf + 1], kw[ts][4 * hf + 2], kw[ts][4 * hf + 3]),
+              bq[2 * wd + hf], sacc[ts], 0, 0, 0);
     }
+    // hi + lo: column c16 < 4 adds column c16 + 4 (row shift by 4 lanes);
+    // only lanes c16 < 4 carry logits from here on
 #pragma unroll
     for (int ts = 0; ts < 4; ++ts) {
+      float v4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v4[i] = sacc[ts][i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v4[i] += row_shl4(v4[i]);
+      sacc[ts] = f4{v4[0], v4[1], v4[2], v4[3]};
       mx = fmaxf(fmaxf(fmaxf(mx, sacc[ts][0]), sacc[ts][1]), fmaxf(sacc[ts][2], sacc[ts][3]));
       if (c16 < 4) *reinterpret_cast<f4*>(&sl[wave][slot][c16][ts * 16 + 4 * g]) = sacc[ts];
     }
   };
 
-  VWin va, vb;
-  if (w_first < w_end) fetch_values(w_first, va);            // first window of pass 2
-  int nslot = 0;
-  {
-    KWin ka, kb;
-    int win = w_first;
-    if (win < wf_end) fetch_keys(win, ka);
-    while (win < wf_end) {
-      if (win + 4 < wf_end) fetch_keys(win + 4, kb);
-      window_logits(ka, nslot++);
-      win += 4;
-      if (win >= wf_end) break;
-      if (win + 4 < wf_end) fetch_keys(win + 4, ka);
-      window_logits(kb, nslot++);
-      win += 4;
-    }
-  }
-  // lanes with equal (lane % 4) hold the same head: reduce within rows by
-  // rotations of 4 and 8, then across the four rows
-  mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, mx), 0x124, 0xF, 0xF, false)));
-  mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, mx), 0x128, 0xF, 0xF, false)));
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  // windows of this wave: w_first + 4k for k < n_mine, the first n_full of
+  // them full; slot k of sl holds window k.  Keys are fetched kKeyAhead
+  // windows ahead, values kValAhead ahead (the first ones during pass 1).
+  const int n_mine = w_first < w_end ? (w_end - w_first + 3) / 4 : 0;
+  const int n_full = w_first < wf_end ? (wf_end - w_first + 3) / 4 : 0;
+  // ================= pass 2 state: p = 2^(l - M), P.V
   float M[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-    M[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), hh));
-  // the unfinished window: bf16 keys from the tail, plain fp32 dot products
-  const int wt = w_first + 4 * nslot;
-  if (wt == n_full_win && wt < w_end) {
-    const int t = wt * kWindow + lane;
-    float lg[G];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) lg[hh] = -__builtin_inff();
-    if (t < t_end) {
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) lg[hh] = 0.0f;
-      const uint16_t* kt = a.ktail + (bh * kWindow + lane) * D;
-#pragma unroll 4
-      for (int v = 0; v < D / 8; ++v) {
-        float x[8];
-        bf16x8_to_f32(*reinterpret_cast<const uint4*>(kt + v * 8), x);
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-          for (int hh = 0; hh < G; ++hh) lg[hh] = __builtin_fmaf(qs[v * 8 + u][hh], x[u], lg[hh]);
-      }
-    }
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      sl[wave][nslot][hh][lane] = lg[hh];
-      M[hh] = fmaxf(M[hh], wave_max(lg[hh]));
-    }
-    ++nslot;
-  }
-  wave_lds_sync();
-
-  // ================= pass 2: p = 2^(l - M), P.V
   float l_lane[G], pz[G][4];
   f4 o[8], ocorr;
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    l_lane[hh] = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) pz[hh][q] = 0.0f;
-  }
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt) o[mt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-  ocorr = f4{0.0f, 0.0f, 0.0f, 0.0f};
   // bases of the value operand: dword j of k-step k2 holds the tokens of
   // code-word positions i = 4 k2 + j and i + 8
   h8 vbase[2];
@@ -651,13 +650,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
       for (int q = 0; q < 4; ++q) {
         const float sc = f16_bits_to_f32(vw[q]), zc = f16_bits_to_f32(vw[q] >> 16);
         pz[hh][q] = __builtin_fmaf(p, zc, pz[hh][q]);
-        pb[wave][4 * q + hh][g][kk][jj] = (_Float16)(p * sc);
+        pb[wave][4 * q + hh][g * 16 + kk * 8 + jj] = (_Float16)(p * sc);
       }
     }
     wave_lds_sync();
     h8 bpv[2];
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) bpv[k2] = *reinterpret_cast<const h8*>(&pb[wave][c16][g][k2][0]);
+    for (int k2 = 0; k2 < 2; ++k2) bpv[k2] = *reinterpret_cast<const h8*>(&pb[wave][c16][g * 16 + k2 * 8]);
 #pragma unroll
     for (int m0 = 0; m0 < 8; m0 += 4) {
       uint32_t vx[4][8];
@@ -675,40 +674,105 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
     ocorr = __builtin_amdgcn_mfma_f32_16x16x32_f16(vbase[1], bpv[1], ocorr, 0, 0, 0);
     wave_lds_sync();
   };
-  {
-    int slot = 0, win = w_first;
-    while (slot < nslot) {
-      if (slot + 1 < nslot) fetch_values(win + 4, vb);
-      window_pv(va, slot);
-      ++slot;
-      win += 4;
-      if (slot >= nslot) break;
-      if (slot + 1 < nslot) fetch_values(win + 4, va);
-      window_pv(vb, slot);
-      ++slot;
-      win += 4;
+  // The whole two-pass walk, instantiated twice: with every window of the
+  // wave full and present (the common case) all loads are unconditional, so
+  // the compiler can wait for exactly the window it needs; guarded loads
+  // would make it wait for every outstanding load at each join.
+  auto run = [&](auto all_full) {
+    constexpr bool F = decltype(all_full)::value;
+    KWin kbuf[MAXW];
+    VWin vbuf[MAXW];
+#pragma unroll
+    for (int k = 0; k < kKeyAhead; ++k)
+      if (F || k < n_full) fetch_keys(w_first + 4 * k, kbuf[k]);
+    // once the key stream is fully requested, the value stream starts
+#pragma unroll
+    for (int k = 0; k < MAXW; ++k) {
+      if (F || k < n_full) {
+        if (k + kKeyAhead < MAXW && (F || k + kKeyAhead < n_full))
+          fetch_keys(w_first + 4 * (k + kKeyAhead), kbuf[(k + kKeyAhead) % MAXW]);
+        else if (F && k + kKeyAhead >= MAXW && k + kKeyAhead - MAXW < kValAhead)
+          fetch_values(w_first + 4 * (k + kKeyAhead - MAXW), vbuf[k + kKeyAhead - MAXW]);
+        window_logits(kbuf[k], k);
+      }
     }
-  }
+    if (!F) {
+#pragma unroll
+      for (int k = 0; k < kValAhead; ++k)
+        if (k < n_mine) fetch_values(w_first + 4 * k, vbuf[k]);
+    }
+    // lane c16 < 4 of each row holds head c16: reduce across the four rows
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+      M[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), hh));
+    // the unfinished window: bf16 keys from the tail, plain fp32 dot products
+    if (!F && n_mine > n_full) {
+      const int wt = w_first + 4 * n_full;
+      const int t = wt * kWindow + lane;
+      float lg[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) lg[hh] = -__builtin_inff();
+      if (t < t_end) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) lg[hh] = 0.0f;
+        const uint16_t* kt = a.ktail + (bh * kWindow + lane) * D;
+#pragma unroll 4
+        for (int v = 0; v < D / 8; ++v) {
+          float x[8];
+          bf16x8_to_f32(*reinterpret_cast<const uint4*>(kt + v * 8), x);
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) lg[hh] = __builtin_fmaf(qs[v * 8 + u][hh], x[u], lg[hh]);
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        sl[wave][n_full][hh][lane] = lg[hh];
+        M[hh] = fmaxf(M[hh], wave_max(lg[hh]));
+      }
+    }
+    wave_lds_sync();
+
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      l_lane[hh] = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pz[hh][q] = 0.0f;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) o[mt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    ocorr = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < MAXW; ++k) {
+      if (F || k < n_mine) {
+        if (k + kValAhead < MAXW && (F || k + kValAhead < n_mine))
+          fetch_values(w_first + 4 * (k + kValAhead), vbuf[(k + kValAhead) % MAXW]);
+        window_pv(vbuf[k], k);
+      }
+    }
+  };
+  if (n_full == MAXW) run(std::true_type{});
+  else run(std::false_type{});
   float m_ref[G];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) m_ref[hh] = nslot > 0 ? M[hh] : -__builtin_inff();
+  for (int hh = 0; hh < G; ++hh) m_ref[hh] = n_mine > 0 ? M[hh] : -__builtin_inff();
 
   // ---- wave partial: lane (col n = 4 q + head, g) keeps channels of group q
   {
     const int hh = c16 & 3, q = c16 >> 2;
-    float lsum[G], zs[G][4];
+    // zq = sum over the wave of pz[hh][q]; row r of ls holds sum l_lane[r]
+    float zv[16];
 #pragma unroll
-    for (int x = 0; x < G; ++x) {
-      lsum[x] = wave_sum(l_lane[x]);
-#pragma unroll
-      for (int y = 0; y < 4; ++y) zs[x][y] = wave_sum(pz[x][y]);
-    }
-    float zq = 0.0f;
+    for (int j = 0; j < 16; ++j) zv[j] = pz[j & 3][j >> 2];
+    const float zq = wave_sum16_at(zv, c16);
+    const float ls = wave_sum4(l_lane);
+    float lsum[G];
 #pragma unroll
     for (int x = 0; x < G; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y)
-        if (x == hh && y == q) zq = zs[x][y];
+      lsum[x] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), 16 * x));
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
       if ((mt >> 1) == q) {
@@ -747,9 +811,12 @@ __global__ __launch_bounds__(128) void decode_reduce_kernel(const float* __restr
                                                             float* __restrict__ lse) {
   __shared__ float xs[D];
   const int r = blockIdx.x, c = threadIdx.x;
+  // unrolled so that the partials' loads are in flight together
   float M = -__builtin_inff();
+#pragma unroll 8
   for (int s = 0; s < S; ++s) M = fmaxf(M, ws[((int64_t)s * BHq + r) * (D + 2) + D]);
   float L = 0.0f, acc = 0.0f;
+#pragma unroll 8
   for (int s = 0; s < S; ++s) {
     const float* p = ws + ((int64_t)s * BHq + r) * (D + 2);
     const float f = exp2f(p[D] - M);
