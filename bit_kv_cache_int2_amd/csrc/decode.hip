@@ -16,8 +16,6 @@
 // wave-shuffle maxima; each block merges its four waves and writes one
 // partial (o, m, l); a second kernel merges the splits, rotates rotated
 // values back and writes out/lse.
-#include <type_traits>
-
 #include "device.h"
 #include "internal.h"
 
@@ -28,6 +26,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Most windows one split (one block) covers: eight per wave.
 constexpr int kDecodeMaxWindows = 32;
+// Resident blocks per CU of the MFMA decode kernel (LDS and register use
+// are sized for three).
+constexpr int kDecodeBlocksPerCU = 3;
 // Fourth word of a raw buffer resource (32-bit data format), and the
 // non-temporal cache policy for streamed cache reads.
 constexpr int kBufferWord3 = 0x00020000;
@@ -469,15 +470,16 @@ KVQ_DEV float wave_sum16_at(const float v[16], int jsel) {
   return __shfl(y, 4 * jsel, 64);
 }
 
-__global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(256, 3) void decode_mfma_kernel(const DecodeArgs a) {
   constexpr int D = 128, G = 4, MAXW = kDecodeMaxWindows / 4;
   __shared__ float qs[D][G];                                   // q * scale * log2 e
-  // LDS strides are padded so that a wave's accesses spread over the 64
-  // banks: qb heads by 4 dwords, sl heads by 16, pb columns by 4
+  // A wave's LDS accesses spread over the 64 banks: qb heads are padded
+  // by 4 dwords, pb columns by 4; sl stores token t of head h at t ^ 16h.
+  // After pass 2 a wave's sl region holds its partial output.
   __shared__ __align__(16) uint32_t qb[4][4][132];             // [wave][head][(hi,lo) g ks] 8 halfs
-  __shared__ __align__(16) float sl[4][MAXW][G][kWave + 16];   // [wave][slot][head][token] logits
+  __shared__ __align__(16) float sl[4][MAXW][G][kWave];        // [wave][slot][head][token ^ 16 head]
   __shared__ __align__(16) _Float16 pb[4][16][72];             // [wave][col][(g kk) 8 halfs]
-  __shared__ float wm[4][G], wlv[4][G], wo[4][G][D];
+  __shared__ float wm[4][G], wlv[4][G];
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   // the wave index is uniform in a wave; saying so keeps window offsets scalar
@@ -513,6 +515,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
       (void*)(a.vcodes + bh * nwin_cap * (int64_t)D * 16), (short)0, nwin_cap * D * 16, kBufferWord3);
   const auto rvp = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.vparams + bh * a.Tcap * 4), (short)0, a.n_tokens * 16, kBufferWord3);
+  // a window past the wave's last one loads through an empty view: the
+  // load instructions stay unconditional (so waits stay exact) and read 0
+  const auto rnone = __builtin_amdgcn_make_buffer_rsrc((void*)a.kcodes, (short)0, 0, kBufferWord3);
 
   // ================= pass 1: logits
   // this lane's channel pair for the query fold: ca and ca + 8, position
@@ -532,16 +537,17 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
     uint32_t pa, pb;   // window parameters of channels ca, cb
   };
   const int ko = c16 * (D / 4) + 8 * g, vo = c16 * 16 + 4 * g;
-  auto fetch_keys = [&](int win, KWin& f) {
+  auto fetch_keys = [&](int win, KWin& f, bool live) {
     const int w = __builtin_amdgcn_readfirstlane(win);
     const int so = w * kWindow * (D / 4), sp = w * D * 4;
+    const auto r0 = live ? rk : rnone, r1 = live ? rkp : rnone;
 #pragma unroll
     for (int ts = 0; ts < 4; ++ts) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rk, ko + ts * 16 * (D / 4), so, kNT);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(r0, ko + ts * 16 * (D / 4), so, kNT);
       f.kc[ts] = make_uint2(v[0], v[1]);
     }
-    f.pa = __builtin_amdgcn_raw_buffer_load_b32(rkp, ca * 4, sp, kNT);
-    f.pb = __builtin_amdgcn_raw_buffer_load_b32(rkp, cb * 4, sp, kNT);
+    f.pa = __builtin_amdgcn_raw_buffer_load_b32(r1, ca * 4, sp, kNT);
+    f.pb = __builtin_amdgcn_raw_buffer_load_b32(r1, cb * 4, sp, kNT);
     // keep each window's loads together and in issue order: the wait for
     // window w then leaves every later window's loads in flight
     __builtin_amdgcn_sched_barrier(0);
@@ -550,13 +556,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
     uint32_t vcw[8];   // value codes: channel mt*16 + c16, tokens 16g .. 16g+15
     uint4 vp;          // value parameters of token lane
   };
-  auto fetch_values = [&](int win, VWin& f) {
+  auto fetch_values = [&](int win, VWin& f, bool live) {
     const int w = __builtin_amdgcn_readfirstlane(win);
     const int so = w * D * 16;
+    const auto r0 = live ? rv : rnone, r1 = live ? rvp : rnone;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
-      f.vcw[mt] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo + mt * 256, so, kNT);
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rvp, lane * 16, w * kWindow * 16, kNT);
+      f.vcw[mt] = __builtin_amdgcn_raw_buffer_load_b32(r0, vo + mt * 256, so, kNT);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r1, lane * 16, w * kWindow * 16, kNT);
     f.vp = make_uint4(v[0], v[1], v[2], v[3]);
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -615,9 +622,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
       for (int i = 0; i < 4; ++i) v4[i] = sacc[ts][i];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v4[i] += row_shl4(v4[i]);
-      sacc[ts] = f4{v4[0], v4[1], v4[2], v4[3]};
-      mx = fmaxf(fmaxf(fmaxf(mx, sacc[ts][0]), sacc[ts][1]), fmaxf(sacc[ts][2], sacc[ts][3]));
-      if (c16 < 4) *reinterpret_cast<f4*>(&sl[wave][slot][c16][ts * 16 + 4 * g]) = sacc[ts];
+      mx = fmaxf(fmaxf(fmaxf(mx, v4[0]), v4[1]), fmaxf(v4[2], v4[3]));
+      if (c16 < 4)
+        *reinterpret_cast<f4*>(&sl[wave][slot][c16][(ts * 16 + 4 * g) ^ (16 * c16)]) = f4{v4[0], v4[1], v4[2], v4[3]};
     }
   };
 
@@ -644,7 +651,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
     const uint32_t vw[4] = {cur.vp.x, cur.vp.y, cur.vp.z, cur.vp.w};
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float p = __builtin_amdgcn_exp2f(sl[wave][slot][hh][lane] - M[hh]);
+      const float p = __builtin_amdgcn_exp2f(sl[wave][slot][hh][lane ^ (16 * hh)] - M[hh]);
       l_lane[hh] += p;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -674,88 +681,72 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
     ocorr = __builtin_amdgcn_mfma_f32_16x16x32_f16(vbase[1], bpv[1], ocorr, 0, 0, 0);
     wave_lds_sync();
   };
-  // The whole two-pass walk, instantiated twice: with every window of the
-  // wave full and present (the common case) all loads are unconditional, so
-  // the compiler can wait for exactly the window it needs; guarded loads
-  // would make it wait for every outstanding load at each join.
-  auto run = [&](auto all_full) {
-    constexpr bool F = decltype(all_full)::value;
-    KWin kbuf[MAXW];
-    VWin vbuf[MAXW];
+  // Loads are unconditional (past-the-end windows read through the empty
+  // view), so the compiler's waits name exactly the window needed next.
+  KWin kbuf[MAXW];
+  VWin vbuf[MAXW];
 #pragma unroll
-    for (int k = 0; k < kKeyAhead; ++k)
-      if (F || k < n_full) fetch_keys(w_first + 4 * k, kbuf[k]);
-    // once the key stream is fully requested, the value stream starts
+  for (int k = 0; k < kKeyAhead; ++k) fetch_keys(w_first + 4 * k, kbuf[k], k < n_full);
+  // once the key stream is fully requested, the value stream starts
 #pragma unroll
-    for (int k = 0; k < MAXW; ++k) {
-      if (F || k < n_full) {
-        if (k + kKeyAhead < MAXW && (F || k + kKeyAhead < n_full))
-          fetch_keys(w_first + 4 * (k + kKeyAhead), kbuf[(k + kKeyAhead) % MAXW]);
-        else if (F && k + kKeyAhead >= MAXW && k + kKeyAhead - MAXW < kValAhead)
-          fetch_values(w_first + 4 * (k + kKeyAhead - MAXW), vbuf[k + kKeyAhead - MAXW]);
-        window_logits(kbuf[k], k);
-      }
-    }
-    if (!F) {
+  for (int k = 0; k < MAXW; ++k) {
+    const int kn = k + kKeyAhead;
+    if (kn < MAXW)
+      fetch_keys(w_first + 4 * kn, kbuf[kn], kn < n_full);
+    else if (kn - MAXW < kValAhead)
+      fetch_values(w_first + 4 * (kn - MAXW), vbuf[kn - MAXW], kn - MAXW < n_mine);
+    if (k < n_full) window_logits(kbuf[k], k);
+  }
+  // lane c16 < 4 of each row holds head c16: reduce across the four rows
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
 #pragma unroll
-      for (int k = 0; k < kValAhead; ++k)
-        if (k < n_mine) fetch_values(w_first + 4 * k, vbuf[k]);
-    }
-    // lane c16 < 4 of each row holds head c16: reduce across the four rows
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  for (int hh = 0; hh < G; ++hh)
+    M[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), hh));
+  // the unfinished window: bf16 keys from the tail, plain fp32 dot products
+  if (n_mine > n_full) {
+    const int wt = w_first + 4 * n_full;
+    const int t = wt * kWindow + lane;
+    float lg[G];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-      M[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), hh));
-    // the unfinished window: bf16 keys from the tail, plain fp32 dot products
-    if (!F && n_mine > n_full) {
-      const int wt = w_first + 4 * n_full;
-      const int t = wt * kWindow + lane;
-      float lg[G];
+    for (int hh = 0; hh < G; ++hh) lg[hh] = -__builtin_inff();
+    if (t < t_end) {
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) lg[hh] = -__builtin_inff();
-      if (t < t_end) {
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) lg[hh] = 0.0f;
-        const uint16_t* kt = a.ktail + (bh * kWindow + lane) * D;
+      for (int hh = 0; hh < G; ++hh) lg[hh] = 0.0f;
+      const uint16_t* kt = a.ktail + (bh * kWindow + lane) * D;
 #pragma unroll 4
-        for (int v = 0; v < D / 8; ++v) {
-          float x[8];
-          bf16x8_to_f32(*reinterpret_cast<const uint4*>(kt + v * 8), x);
+      for (int v = 0; v < D / 8; ++v) {
+        float x[8];
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(kt + v * 8), x);
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 8; ++u)
 #pragma unroll
-            for (int hh = 0; hh < G; ++hh) lg[hh] = __builtin_fmaf(qs[v * 8 + u][hh], x[u], lg[hh]);
-        }
-      }
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        sl[wave][n_full][hh][lane] = lg[hh];
-        M[hh] = fmaxf(M[hh], wave_max(lg[hh]));
+          for (int hh = 0; hh < G; ++hh) lg[hh] = __builtin_fmaf(qs[v * 8 + u][hh], x[u], lg[hh]);
       }
     }
-    wave_lds_sync();
-
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      l_lane[hh] = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) pz[hh][q] = 0.0f;
+      sl[wave][n_full][hh][lane ^ (16 * hh)] = lg[hh];
+      M[hh] = fmaxf(M[hh], wave_max(lg[hh]));
     }
+  }
+  wave_lds_sync();
+
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) o[mt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    ocorr = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int hh = 0; hh < G; ++hh) {
+    l_lane[hh] = 0.0f;
 #pragma unroll
-    for (int k = 0; k < MAXW; ++k) {
-      if (F || k < n_mine) {
-        if (k + kValAhead < MAXW && (F || k + kValAhead < n_mine))
-          fetch_values(w_first + 4 * (k + kValAhead), vbuf[(k + kValAhead) % MAXW]);
-        window_pv(vbuf[k], k);
-      }
-    }
-  };
-  if (n_full == MAXW) run(std::true_type{});
-  else run(std::false_type{});
+    for (int q = 0; q < 4; ++q) pz[hh][q] = 0.0f;
+  }
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) o[mt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  ocorr = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int k = 0; k < MAXW; ++k) {
+    const int kn = k + kValAhead;
+    if (kn < MAXW) fetch_values(w_first + 4 * kn, vbuf[kn], kn < n_mine);
+    if (k < n_mine) window_pv(vbuf[k], k);
+  }
   float m_ref[G];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) m_ref[hh] = n_mine > 0 ? M[hh] : -__builtin_inff();
@@ -773,13 +764,18 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int x = 0; x < G; ++x)
       lsum[x] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), 16 * x));
+    // this lane's tiles are 2q and 2q + 1 (the channels of its group)
+    f4 oa = o[0], ob = o[1];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      if ((mt >> 1) == q) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) wo[wave][hh][mt * 16 + 4 * g + i] = o[mt][i] - ocorr[i] + zq;
+    for (int qq = 1; qq < 4; ++qq)
+      if (q == qq) {
+        oa = o[2 * qq];
+        ob = o[2 * qq + 1];
       }
-    }
+    const f4 cz = ocorr - zq;
+    float* wo = &sl[wave][0][0][0] + hh * D + 32 * q + 4 * g;
+    *reinterpret_cast<f4*>(wo) = oa - cz;
+    *reinterpret_cast<f4*>(wo + 16) = ob - cz;
     if (lane < G) {
       wm[wave][lane] = m_ref[lane];
       wlv[wave][lane] = lsum[lane];
@@ -794,8 +790,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
     float acc = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float f = (wm[w][hh] == -__builtin_inff()) ? 0.0f : exp2f(wm[w][hh] - M);
-      const float v = (c < D) ? wo[w][hh][c] : wlv[w][hh];
+      const float f = (wm[w][hh] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(wm[w][hh] - M);
+      const float v = (c < D) ? (&sl[w][0][0][0])[hh * D + c] : wlv[w][hh];
       acc = __builtin_fmaf(f, v, acc);
     }
     float* dst = a.ws + (((int64_t)s * gridDim.z + b) * a.Hq + hq0 + hh) * (D + 2);
@@ -883,17 +879,37 @@ hipError_t launch_partial_g(const DecodeArgs& a, int G, int key_mode, int R, int
 
 }  // namespace
 
+// Splits per (sequence, kv head).  A split covers at most
+// kDecodeMaxWindows windows; among the admissible counts the one that fills
+// the device's resident block slots in the fewest, fullest rounds wins
+// (cost = rounds x (windows per split + 2 windows of per-block overhead)).
 int decode_splits(const kvq_layout* L, int q_heads, int n_tokens) {
   (void)q_heads;
   const int n_win = (n_tokens + kWindow - 1) / kWindow;
-  const int units = L->batch * L->kv_heads;
-  int S = (2048 + units - 1) / units;
-  if (S > n_win) S = n_win;
+  if (n_win <= 0) return 1;
+  const int64_t units = (int64_t)L->batch * L->kv_heads;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+  }
+  const int64_t slots = (int64_t)cus * kDecodeBlocksPerCU;
   const int s_min = (n_win + kDecodeMaxWindows - 1) / kDecodeMaxWindows;
-  if (S < s_min) S = s_min;
-  if (S < 1) S = 1;
-  const int per = (n_win + S - 1) / S;
-  return (n_win + per - 1) / per;
+  const int s_max = n_win < s_min * 16 ? n_win : s_min * 16;
+  int best = s_min;
+  double best_cost = 1e300;
+  for (int S = s_min; S <= s_max; ++S) {
+    const int per = (n_win + S - 1) / S;
+    if ((n_win + per - 1) / per != S) continue;     // same partition as a smaller S
+    const double rounds = (double)((units * S + slots - 1) / slots);
+    const double cost = rounds * (per + 2.0);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = S;
+    }
+  }
+  return best;
 }
 
 size_t decode_workspace_bytes(const kvq_layout* L, int q_heads, int n_tokens) {
