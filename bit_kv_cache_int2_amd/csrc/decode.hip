@@ -807,17 +807,39 @@ __global__ __launch_bounds__(128) void decode_reduce_kernel(const float* __restr
                                                             float* __restrict__ lse) {
   __shared__ float xs[D];
   const int r = blockIdx.x, c = threadIdx.x;
-  // unrolled so that the partials' loads are in flight together
-  float M = -__builtin_inff();
-#pragma unroll 8
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ws[((int64_t)s * BHq + r) * (D + 2) + D]);
-  float L = 0.0f, acc = 0.0f;
-#pragma unroll 8
-  for (int s = 0; s < S; ++s) {
-    const float* p = ws + ((int64_t)s * BHq + r) * (D + 2);
-    const float f = exp2f(p[D] - M);
-    L = __builtin_fmaf(f, p[D + 1], L);
-    if (c < D) acc = __builtin_fmaf(f, p[c], acc);
+  // Splits are merged in chunks of 16: every load of a chunk is issued
+  // before any is used (one memory round trip per chunk), and the running
+  // (M, L, acc) is rescaled once per chunk.
+  float M = -__builtin_inff(), L = 0.0f, acc = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += 16) {
+    float mv[16], lv[16], pv[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int s = s0 + k;
+      mv[k] = -__builtin_inff();
+      lv[k] = 0.0f;
+      pv[k] = 0.0f;
+      if (s < S) {
+        const float* p = ws + ((int64_t)s * BHq + r) * (D + 2);
+        mv[k] = p[D];
+        lv[k] = p[D + 1];
+        if (c < D) pv[k] = p[c];
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) Mn = fmaxf(Mn, mv[k]);
+    if (Mn == -__builtin_inff()) continue;
+    const float sc = (M == -__builtin_inff()) ? 0.0f : exp2f(M - Mn);
+    L *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float f = (mv[k] == -__builtin_inff()) ? 0.0f : exp2f(mv[k] - Mn);
+      L = __builtin_fmaf(f, lv[k], L);
+      acc = __builtin_fmaf(f, pv[k], acc);
+    }
+    M = Mn;
   }
   float v = acc / L;
   if (HAD) {

@@ -77,6 +77,29 @@ def test_window_decode_bf16_output_and_determinism():
     assert torch.equal(a, a2)
 
 
+def test_window_decode_reused_workspace():
+    """Rotated values with window keys against the oracle, then one
+    workspace reused across calls of different lengths: every call matches
+    a call on a fresh workspace bit for bit."""
+    d = synth.llm_decode(B=2, Hkv=2, Hq=8, D=128, T=3000)
+    c = kv.KVCache(2, 2, 128, 3008, value_mode=kv.VAL_HADAMARD)
+    o = oracle_like(c)
+    kv.kv_quantize_append(c, dev_bf16(d["K"]), dev_bf16(d["V"]), 0)
+    o.append(d["K"], d["V"], 0)
+    qd = dev_bf16(d["q"])
+    q64 = synth.bf16_bits_to_f32(d["q"]).astype(np.float64)
+    _decode_check(c, o, 3000, qd, q64, 1 / math.sqrt(128), "rotated values")
+    ws = kv.decode_workspace(c, 8, 3000)
+    for n in (3000, 700, 64, 3000, 1999):
+        lse_a = torch.empty(16, dtype=torch.float32, device="cuda")
+        lse_b = torch.empty(16, dtype=torch.float32, device="cuda")
+        a = kv.attn_int2_decode(c, n, qd, 1 / math.sqrt(128), lse=lse_a, workspace=ws)
+        b = kv.attn_int2_decode(c, n, qd, 1 / math.sqrt(128), lse=lse_b)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), f"n={n}"
+        assert torch.equal(lse_a, lse_b), f"n={n}"
+
+
 @pytest.mark.parametrize("mode,R,had", [(kv.KEY_CENTROID, 0, True), (kv.KEY_CENTROID_QSAC, 8, True),
                                         (kv.KEY_CENTROID_QSAC, 8, False)])
 def test_centroid_decode_psac_hadamard(mode, R, had):
