@@ -23,6 +23,8 @@ the chunk attention of a query frame (or frames) against the packed history
 plus, for long_history and video_chunk, the quantize-append of that
 frame's own keys and values; `value` is then the attention's algorithmic
 TFLOP/s (4 * q_len * n_tokens * head_dim * heads per call).
+--workload copy runs a plain 1 GiB elementwise copy, the reference for scaling
+rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes.
 """
 from __future__ import annotations
 
@@ -55,9 +57,13 @@ CACHE_BYTES = (B * HKV * T * D // 4          # key codes
 APPEND_BYTES = APPEND_READ + CACHE_BYTES
 DECODE_BYTES = CACHE_BYTES + B * HQ * D * 2 + B * HQ * D * 4
 
-COUNTERS = os.path.join(ROOT, "profiles", "window_append_llm_decode_counters.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "bit_kv_cache_int2_amd", "csrc", f)
-                  for f in ("quantize.hip", "device.h")]
+COPY_BYTES = 1 << 30
+CSRC = os.path.join(ROOT, "bit_kv_cache_int2_amd", "csrc")
+# committed rocprofv3 counter summaries: (file, sources the counters were taken on)
+APPEND_COUNTERS = (os.path.join(ROOT, "profiles", "tile_append_llm_decode_counters.txt"),
+                   [os.path.join(CSRC, f) for f in ("quantize.hip", "device.h")])
+DECODE_COUNTERS = (os.path.join(ROOT, "profiles", "decode_mfma_llm_decode_counters.txt"),
+                   [os.path.join(CSRC, f) for f in ("decode.hip", "device.h")])
 
 
 def _source_hash(paths) -> str:
@@ -68,23 +74,43 @@ def _source_hash(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def _counter_traffic():
-    """HBM bytes per append launch from the committed rocprofv3 counter
-    summary, or None when it is missing or was taken on other kernel code."""
-    if not os.path.exists(COUNTERS):
+def _counter_traffic(spec):
+    """HBM bytes per launch from a committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's counters), or None
+    when it is missing or was taken on other kernel code."""
+    path, sources = spec
+    if not os.path.exists(path):
         return None
     kv = {}
-    with open(COUNTERS) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
     try:
-        if kv.get("source_sha256") != _source_hash(KERNEL_SOURCES):
+        if kv.get("source_sha256") != _source_hash(sources):
             return None
         return float(kv["hbm_bytes_per_dispatch"])
     except (KeyError, ValueError):
         return None
+
+
+def copy_calibration(steps: int) -> int:
+    """A plain elementwise kernel over COPY_BYTES (dst = ~src: each byte
+    read once and written once per launch), for scaling rocprofv3's
+    FETCH_SIZE and WRITE_SIZE counters to bytes.  (A same-dtype copy_ would
+    go to the copy engine, which the counters do not see.)"""
+    import torch
+
+    torch.cuda.set_device(0)
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(max(steps, 1)):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": "copy", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                      "launches": max(steps, 1)}), flush=True)
+    return 0
 
 
 def cpu_baseline(d) -> dict:
@@ -219,12 +245,14 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="llm_decode",
-                    choices=["llm_decode", "long_history", "video_chunk", "sensitivity"])
+                    choices=["llm_decode", "long_history", "video_chunk", "sensitivity", "copy"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the path has no multi-GPU leg "
               "(sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
         return 2
+    if args.workload == "copy":
+        return copy_calibration(args.steps)
     if args.workload != "llm_decode":
         import torch
         torch.cuda.set_device(0)
@@ -276,7 +304,8 @@ def main() -> int:
     value = (APPEND_BYTES + DECODE_BYTES) * args.steps / wall / 1e9
     app_gbs = APPEND_BYTES / t_app / 1e9
     dec_gbs = DECODE_BYTES / t_dec / 1e9
-    traffic = _counter_traffic()
+    traffic = _counter_traffic(APPEND_COUNTERS)
+    traffic_dec = _counter_traffic(DECODE_COUNTERS)
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
@@ -298,7 +327,8 @@ def main() -> int:
                      "frac": round(app_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
         "roofline_decode": {"kernel": "decode_mfma_kernel + decode_reduce_kernel",
                             "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4)},
+                            "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                            "traffic": traffic_dec},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(d)
