@@ -16,6 +16,7 @@
 // wave-shuffle maxima; each block merges its four waves and writes one
 // partial (o, m, l); a second kernel merges the splits, rotates rotated
 // values back and writes out/lse.
+#include "code_operand.h"
 #include "device.h"
 #include "internal.h"
 
@@ -369,43 +370,6 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
 // products.  Pass 2 streams the value codes and accumulates p = 2^(l - m)
 // <= 1: no running rescale.  Each pass loads window w + 4 while it
 // computes window w.
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-
-// (t & mask) | bits.  gfx9 VOP3 encodings take no literal constants and at
-// most one scalar operand, so v_and_or_b32 needs one of the constants in a
-// VGPR: the bits arrive through an empty asm statement, which hides their
-// value and makes the compiler keep them in a register.
-KVQ_DEV uint32_t and_or(uint32_t t, uint32_t mask, uint32_t bits) { return (t & mask) | bits; }
-
-// Operand dwords for the 16 codes of word d: out[i] holds codes (i, i + 8)
-// in its (low, high) half as base_i + code.  No bit of one half reaches the
-// selected bits of the other: a left shift by 6 moves the low half to bits
-// 6..21 (the high half's codes sit at 22 and up), a right shift by 6 moves
-// the high half to bits 10..25 (the low half's codes end at bit 9).
-struct CodeOr {
-  uint32_t b64, b16, b4;   // exponent bits of 64, 16 and 4 in both halves
-};
-KVQ_DEV void code_word(uint32_t d, const CodeOr& k, uint32_t out[8]) {
-  const uint32_t l6 = d << 6, r6 = d >> 6;
-  out[0] = and_or(l6, 0x00C000C0u, k.b16);
-  out[1] = and_or(l6, 0x03000300u, k.b4);
-  out[2] = and_or(d, 0x00300030u, k.b64);
-  out[3] = and_or(d, 0x00C000C0u, k.b16);
-  out[4] = and_or(d, 0x03000300u, k.b4);
-  out[5] = and_or(r6, 0x00300030u, k.b64);
-  out[6] = and_or(r6, 0x00C000C0u, k.b16);
-  out[7] = and_or(r6, 0x03000300u, k.b4);
-}
-
-// Base of code-word position i.
-KVQ_DEV float code_base(int i) {
-  return (i == 2 || i == 5) ? 64.0f : ((i == 1 || i == 4 || i == 7) ? 4.0f : 16.0f);
-}
-
-KVQ_DEV h8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  return __builtin_bit_cast(h8, make_uint4(a, b, c, d));
-}
 
 // Sums four per-lane values over the wave: afterwards every lane of row r
 // (lanes 16r .. 16r + 15) holds the total of v[r].  Each xor exchange
