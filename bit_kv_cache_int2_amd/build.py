@@ -27,11 +27,12 @@ FLAGS = [
 
 SOURCES = ["api.cpp", "quantize.hip", "decode.hip", "chunk.hip"]
 
-# Per-source extras for the decode kernels: MFMA accumulators in VGPRs (no
-# copies between register files), and no NaN operands (attention never
-# produces one from finite cache contents), which lets max chains compile
-# to v_max3_f32 without quieting each MFMA result first.
-EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
+# Per-source extras for the attention kernels: MFMA accumulators in VGPRs
+# for decode (no copies between register files), and no NaN operands
+# (attention never produces one from finite cache contents), which lets max
+# chains compile to v_max3_f32 without quieting each MFMA result first.
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+         "chunk.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -28,6 +28,8 @@
 // k-step.  Rotated values ([OKV]) are rotated back in registers at the end.
 // When the row blocks alone would not fill the device, the cached tokens
 // are split over blocks and a merge kernel combines the partial (o, m, l).
+#include <type_traits>
+
 #include "code_operand.h"
 #include "device.h"
 #include "internal.h"
@@ -220,10 +222,12 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
     prefetch_cent(pre);
   }
 
-  for (int tile = tile_begin; tile < tile_end; ++tile) {
+  // One 64-token tile; the ragged last tile (masking, key tail) is a
+  // separate instantiation so that full tiles carry no masking code.
+  auto tile_step = [&](int tile, auto ragged) {
     const int t0 = tile * 64;
-    const bool last = tile == n_tiles - 1 && (n & 63) != 0;   // ragged tile
-    const bool full_keys = KM != 0 || tile < n_full;
+    constexpr bool last = decltype(ragged)::value;    // the ragged last tile
+    const bool full_keys = KM != 0 || !last;          // window keys: tail window
     __syncthreads();  // the previous tile's LDS tiles are consumed
     // ---- parameters -> LDS
     if (tid < 64 * NG) vpar[tid % NG][tid / NG] = pre.vp;
@@ -358,6 +362,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
 
     // ---- online softmax (base 2); lane owns row nt*16 + c16, tokens ts*16 + 4g + i
     h8 pb[kNT][2];
+    float alpha[kNT];
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
       if (last) {
@@ -374,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float mn = fmaxf(m_run[nt], mx * a.scale_log2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - mn);
+      alpha[nt] = __builtin_amdgcn_exp2f(m_run[nt] - mn);   // exactly 1 when unchanged
       m_run[nt] = mn;
       uint32_t pw[8];
 #pragma unroll
@@ -388,9 +393,15 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
       // k-step kk takes slabs 2 kk and 2 kk + 1
       pb[nt][0] = as_h8(pw[0], pw[1], pw[2], pw[3]);
       pb[nt][1] = as_h8(pw[4], pw[5], pw[6], pw[7]);
-      ol[nt] *= alpha;
+    }
+    // rescale only when some row of the wave has a new maximum
+    if (__any(alpha[0] != 1.0f || alpha[kNT - 1] != 1.0f)) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[nt][dt] *= alpha;
+      for (int nt = 0; nt < kNT; ++nt) {
+        ol[nt] *= alpha[nt];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[nt][dt] *= alpha[nt];
+      }
     }
 
     // ---- O^T += Vhat^T P^T, l += 1^T P^T
@@ -407,7 +418,11 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
       for (int nt = 0; nt < kNT; ++nt)
         ol[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[nt][kk], ol[nt], 0, 0, 0);
     }
-  }
+  };
+  const bool has_ragged = (n & 63) != 0 && tile_end == n_tiles && tile_begin < tile_end;
+  const int tile_stop = has_ragged ? tile_end - 1 : tile_end;
+  for (int tile = tile_begin; tile < tile_stop; ++tile) tile_step(tile, std::false_type{});
+  if (has_ragged) tile_step(tile_end - 1, std::true_type{});
 
   // ---- epilogue: l of row c16 sits in lane c16 (row 0 of the ones tile)
 #pragma unroll
