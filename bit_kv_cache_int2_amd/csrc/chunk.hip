@@ -21,11 +21,13 @@
 //                    the softmax denominators from the same fp16 P).
 // Each lane owns whole query rows, so the online-softmax max needs only two
 // cross-lane steps; probabilities are 2^(s * scale log2 e - m) with the
-// hardware exp2.  Precision: fp16 operands with fp32 accumulation;
-// window-range keys (whose per-channel scales make logits large) are split
-// as Khat = hi + lo, both fp16, and multiplied twice; centroid keys use one
-// fp16 copy.  PSAC ([QWM] 2) adds (U^T q) . a as one more 16x16x16 MFMA
-// k-step.  Rotated values ([OKV]) are rotated back in registers at the end.
+// hardware exp2, where m is a reference maximum that is raised (and O, l
+// rescaled) only when a probability relative to it would exceed 2^8.
+// Precision: fp16 operands with fp32 accumulation; window-range keys
+// (whose per-channel scales make logits large) are split as Khat = hi + lo,
+// both fp16, and multiplied twice; centroid keys use one fp16 copy.  PSAC
+// ([QWM] 2) adds (U^T q) . a as one more MFMA k-step (k 0..7).  Rotated
+// values ([OKV]) are rotated back in registers at the end.
 // When the row blocks alone would not fill the device, the cached tokens
 // are split over blocks and a merge kernel combines the partial (o, m, l).
 #include <type_traits>
@@ -45,6 +47,8 @@ constexpr int kWaves = 8;
 constexpr int kNT = 2;                       // 16-row query tiles per wave
 constexpr int kBM = kWaves * kNT * 16;      // query rows per block
 constexpr int kThreads = kWaves * kWave;
+// a row's reference maximum may trail its true maximum by this much (log2)
+constexpr float kLazyLog2 = 8.0f;
 
 struct ChunkArgs {
   const uint8_t* kcodes;
@@ -132,25 +136,27 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
       qreg[nt][ks] = v;
     }
   }
-  // ---- PSAC: q' = U^T q (lane supplies q'[4g .. 4g+3] of its row, g < 2)
-  h4 qp[kNT];
+  // ---- PSAC: q' = U^T q, the B operand of one more 16x16x32 k-step: lanes
+  // g == 0 supply q'[0 .. R-1] of their row, every other k is zero
+  static_assert(R == 0 || R == 8, "PSAC rank 8 fills k 0..7 of one k-step");
+  h8 qp[kNT];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qp[nt][j] = (_Float16)0.0f;
+    for (int j = 0; j < 8; ++j) qp[nt][j] = (_Float16)0.0f;
     if (R > 0) {
       const int row = row0 + nt * 16 + c16;
-      if (g < 2 && row < a.Lq) {
+      if (g == 0 && row < a.Lq) {
         const uint16_t* qr = a.q + (((int64_t)b * a.Lq + row) * a.Hq + hq) * D;
         const float* U = a.basis + bh * D * (R > 0 ? R : 1);
-        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
         for (int d = 0; d < D; ++d) {
           const float qd = bf16_to_f32(qr[d]);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(U[d * R + 4 * g + j], qd, acc[j]);
+          for (int j = 0; j < 8; ++j) acc[j] = __builtin_fmaf(U[d * R + j], qd, acc[j]);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) qp[nt][j] = (_Float16)acc[j];
+        for (int j = 0; j < 8; ++j) qp[nt][j] = (_Float16)acc[j];
       }
     }
   }
@@ -339,6 +345,14 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
       for (int ts = 0; ts < 4; ++ts) s[nt][ts] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ts = 0; ts < 4; ++ts) {
+      if (R > 0) {
+        // PSAC first: k 0..7 are token ts*16 + c16's coefficients (lanes
+        // g == 1 read the zero half of the row, g >= 2 meet a zero q')
+        const h8 ca = *reinterpret_cast<const h8*>(&coef[(ts * 16 + c16) * 16 + 8 * (g & 1)]);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+          s[nt][ts] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca, qp[nt], s[nt][ts], 0, 0, 0);
+      }
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const h8 ka = *reinterpret_cast<const h8*>(&khi[(ts * 16 + c16) * KP + ks * 32 + 8 * g]);
@@ -352,17 +366,15 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
             s[nt][ts] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kl, qreg[nt][ks], s[nt][ts], 0, 0, 0);
         }
       }
-      if (R > 0) {
-        const h4 ca = *reinterpret_cast<const h4*>(&coef[(ts * 16 + c16) * 16 + 4 * g]);
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt)
-          s[nt][ts] = __builtin_amdgcn_mfma_f32_16x16x16f16(ca, qp[nt], s[nt][ts], 0, 0, 0);
-      }
     }
 
-    // ---- online softmax (base 2); lane owns row nt*16 + c16, tokens ts*16 + 4g + i
-    h8 pb[kNT][2];
-    float alpha[kNT];
+    // ---- online softmax (base 2); lane owns row nt*16 + c16, tokens ts*16 + 4g + i.
+    // A row's reference maximum moves only when a score passes it by more than
+    // kLazyLog2, so p stays at most 2^kLazyLog2 (exact in fp16's range) and the
+    // rescale of O and l is rare; the exponentials then feed the PV products
+    // without a branch between them.
+    float mx[kNT];
+    bool grow = false;
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
       if (last) {
@@ -372,36 +384,41 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
           for (int i = 0; i < 4; ++i)
             if (t0 + ts * 16 + 4 * g + i >= n) s[nt][ts][i] = -__builtin_inff();
       }
-      float mx = -__builtin_inff();
+      float m = -__builtin_inff();
 #pragma unroll
       for (int ts = 0; ts < 4; ++ts)
-        mx = fmaxf(fmaxf(mx, fmaxf(s[nt][ts][0], s[nt][ts][1])), fmaxf(s[nt][ts][2], s[nt][ts][3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m_run[nt], mx * a.scale_log2);
-      alpha[nt] = __builtin_amdgcn_exp2f(m_run[nt] - mn);   // exactly 1 when unchanged
-      m_run[nt] = mn;
+        m = fmaxf(fmaxf(m, fmaxf(s[nt][ts][0], s[nt][ts][1])), fmaxf(s[nt][ts][2], s[nt][ts][3]));
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      mx[nt] = m * a.scale_log2;
+      grow |= mx[nt] > m_run[nt] + kLazyLog2;
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        const float mn = fmaxf(m_run[nt], mx[nt]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - mn);   // 0 on the first tile
+        m_run[nt] = mn;
+        ol[nt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[nt][dt] *= alpha;
+      }
+    }
+    h8 pb[kNT][2];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
       uint32_t pw[8];
 #pragma unroll
       for (int ts = 0; ts < 4; ++ts)
 #pragma unroll
         for (int i = 0; i < 4; i += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nt][ts][i], a.scale_log2, -mn));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nt][ts][i + 1], a.scale_log2, -mn));
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nt][ts][i], a.scale_log2, -m_run[nt]));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nt][ts][i + 1], a.scale_log2, -m_run[nt]));
           pw[ts * 2 + i / 2] = pk_rne(p0, p1);
         }
       // k-step kk takes slabs 2 kk and 2 kk + 1
       pb[nt][0] = as_h8(pw[0], pw[1], pw[2], pw[3]);
       pb[nt][1] = as_h8(pw[4], pw[5], pw[6], pw[7]);
-    }
-    // rescale only when some row of the wave has a new maximum
-    if (__any(alpha[0] != 1.0f || alpha[kNT - 1] != 1.0f)) {
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        ol[nt] *= alpha[nt];
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[nt][dt] *= alpha[nt];
-      }
     }
 
     // ---- O^T += Vhat^T P^T, l += 1^T P^T
