@@ -19,10 +19,11 @@
 //                    the eight P values it must supply),
 //   l   += 1^T P^T   (one more MFMA against an all-ones operand row gives
 //                    the softmax denominators from the same fp16 P).
-// Each lane owns whole query rows, so the online-softmax max needs only two
-// cross-lane steps; probabilities are 2^(s * scale log2 e - m) with the
-// hardware exp2, where m is a reference maximum that is raised (and O, l
-// rescaled) only when a probability relative to it would exceed 2^8.
+// Probabilities are 2^(s * scale log2 e - m) with the hardware exp2, where
+// m is a per-row reference maximum that is raised (and O, l rescaled) only
+// when a probability relative to it would exceed 2^8; each lane tests its
+// own scores, and the two cross-lane steps of a row maximum are taken only
+// when some row of the wave moves.
 // Precision: fp16 operands with fp32 accumulation; window-range keys
 // (whose per-channel scales make logits large) are split as Khat = hi + lo,
 // both fp16, and multiplied twice; centroid keys use one fp16 copy.  PSAC
@@ -86,8 +87,12 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
   constexpr int NKS = D / 32;        // QK k-steps
   constexpr int NDT = D / 16;        // PV output dim tiles
   constexpr bool LO = (KM == 0);     // hi/lo split keys
-  constexpr int KP = D + 8;          // key tile pitch (halfs)
-  constexpr int VP = 64 + 8;         // value tile pitch (halfs)
+  // Tile pitches of 2 (mod 4) 16-byte units let the sixteen rows one operand
+  // read touches fall on distinct banks; odd key rows and every other pair
+  // of value rows swap neighbouring 16-byte units, which spreads the tile
+  // stores over all banks as well.
+  constexpr int KP = D + 16;         // key tile pitch (halfs)
+  constexpr int VP = 64 + 16;        // value tile pitch (halfs)
   constexpr int NG = D / kGroup;     // parameter groups per row
   constexpr int KW = D / 16;         // key code words (16 channels) per token
   constexpr int NKT = 64 * KW;       // key words per tile
@@ -161,11 +166,15 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
     }
   }
 
-  float m_run[kNT];
+  // m_run: reference maximum (log2 units); thr: the raw score above which it
+  // moves, (m_run + kLazyLog2) / scale_log2
+  float m_run[kNT], thr[kNT];
+  const float inv_scale_log2 = 1.0f / a.scale_log2;
   f4 o[kNT][NDT], ol[kNT];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
     m_run[nt] = -__builtin_inff();
+    thr[nt] = -__builtin_inff();
     ol[nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[nt][dt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -176,8 +185,10 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
   for (int j = 0; j < 8; ++j) ones[j] = (_Float16)(c16 == 0 ? 1.0f : 0.0f);
 
   // ---- per-thread share of a tile: key word = token tk, channels
-  // 16 kw .. 16 kw + 15; value word = channel vc, tokens 16 vq .. 16 vq + 15
-  const int tk = tid / KW, kw = tid % KW;
+  // 16 kw .. 16 kw + 15 (each group of eight lanes holds two tokens);
+  // value word = channel vc, tokens 16 vq .. 16 vq + 15
+  const int tk = KW == 8 ? 2 * (tid >> 4) + ((tid >> 2) & 1) : tid / KW;
+  const int kw = KW == 8 ? (tid & 3) + 4 * ((tid >> 3) & 1) : tid % KW;
   const int vc = tid >> 2, vq = tid & 3;
   const bool has_k = tid < NKT, has_v = tid < NVT;
   struct Pre {
@@ -188,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
   auto prefetch = [&](int tile, Pre& f) {
     const int t0 = tile * 64;
     const int64_t rowbase = bh * a.Tcap + t0;
-    f.kcw = has_k ? reinterpret_cast<const uint32_t*>(a.kcodes + rowbase * (D / 4))[tid] : 0u;
+    f.kcw = has_k ? reinterpret_cast<const uint32_t*>(a.kcodes + rowbase * (D / 4))[tk * KW + kw] : 0u;
     f.vcw = has_v ? reinterpret_cast<const uint32_t*>(
                         a.vcodes + (bh * (a.Tcap / 64) + tile) * (int64_t)D * 16)[tid]
                   : 0u;
@@ -300,13 +311,13 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
           lw[m] = pk_rne(kv[2 * m] - (float)hh[0], kv[2 * m + 1] - (float)hh[1]);
         }
       }
-      uint4* dh = reinterpret_cast<uint4*>(&khi[tk * KP + 16 * kw]);
-      dh[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      dh[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+      // 16-byte units 2 kw, 2 kw + 1 of row tk, swapped in odd rows
+      const int o0 = tk * KP + 8 * ((2 * kw) ^ (tk & 1)), o1 = tk * KP + 8 * ((2 * kw + 1) ^ (tk & 1));
+      *reinterpret_cast<uint4*>(&khi[o0]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *reinterpret_cast<uint4*>(&khi[o1]) = make_uint4(hw[4], hw[5], hw[6], hw[7]);
       if (LO) {
-        uint4* dl = reinterpret_cast<uint4*>(&klo[tk * KP + 16 * kw]);
-        dl[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        dl[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+        *reinterpret_cast<uint4*>(&klo[o0]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        *reinterpret_cast<uint4*>(&klo[o1]) = make_uint4(lw[4], lw[5], lw[6], lw[7]);
       }
     }
     // the next tile's centroid rows (its indices were requested above)
@@ -329,10 +340,12 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
         vv[u] = fma_code(cw[i], u >= 8, s, __builtin_fmaf(-code_base(i), s, z));
       }
       // tokens 16 vq + 4 gg + j: k-step vq / 2, positions 8 gg + 4 (vq & 1) + j
+      // (16-byte units swapped in pairs when bit 1 of the row is set)
       _Float16* dst = &vt[vc * VP + 32 * (vq >> 1) + 4 * (vq & 1)];
+      const int vs = (vc >> 1) & 1;
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg)
-        *reinterpret_cast<uint2*>(dst + 8 * gg) =
+        *reinterpret_cast<uint2*>(dst + 8 * (gg ^ vs)) =
             make_uint2(pk_rne(vv[4 * gg], vv[4 * gg + 1]), pk_rne(vv[4 * gg + 2], vv[4 * gg + 3]));
     }
     __syncthreads();
@@ -355,12 +368,12 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
       }
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const h8 ka = *reinterpret_cast<const h8*>(&khi[(ts * 16 + c16) * KP + ks * 32 + 8 * g]);
+        const h8 ka = *reinterpret_cast<const h8*>(&khi[(ts * 16 + c16) * KP + ks * 32 + 8 * (g ^ (c16 & 1))]);
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt)
           s[nt][ts] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qreg[nt][ks], s[nt][ts], 0, 0, 0);
         if (LO) {
-          const h8 kl = *reinterpret_cast<const h8*>(&klo[(ts * 16 + c16) * KP + ks * 32 + 8 * g]);
+          const h8 kl = *reinterpret_cast<const h8*>(&klo[(ts * 16 + c16) * KP + ks * 32 + 8 * (g ^ (c16 & 1))]);
 #pragma unroll
           for (int nt = 0; nt < kNT; ++nt)
             s[nt][ts] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kl, qreg[nt][ks], s[nt][ts], 0, 0, 0);
@@ -369,11 +382,12 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
     }
 
     // ---- online softmax (base 2); lane owns row nt*16 + c16, tokens ts*16 + 4g + i.
-    // A row's reference maximum moves only when a score passes it by more than
-    // kLazyLog2, so p stays at most 2^kLazyLog2 (exact in fp16's range) and the
-    // rescale of O and l is rare; the exponentials then feed the PV products
-    // without a branch between them.
-    float mx[kNT];
+    // A row's reference maximum m (the same in the four lanes of the row)
+    // moves only when a score passes it by more than kLazyLog2, so p stays at
+    // most 2^kLazyLog2 (well inside fp16) and O, l are rescaled rarely.  The
+    // test needs only the lane's own scores; the row maximum across lanes is
+    // formed only when some row of the wave moves.
+    float lm[kNT];
     bool grow = false;
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
@@ -388,17 +402,19 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
 #pragma unroll
       for (int ts = 0; ts < 4; ++ts)
         m = fmaxf(fmaxf(m, fmaxf(s[nt][ts][0], s[nt][ts][1])), fmaxf(s[nt][ts][2], s[nt][ts][3]));
-      m = fmaxf(m, __shfl_xor(m, 16, 64));
-      m = fmaxf(m, __shfl_xor(m, 32, 64));
-      mx[nt] = m * a.scale_log2;
-      grow |= mx[nt] > m_run[nt] + kLazyLog2;
+      lm[nt] = m;
+      grow |= m > thr[nt];
     }
     if (__any(grow)) {
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
-        const float mn = fmaxf(m_run[nt], mx[nt]);
+        float m = lm[nt];
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        const float mn = fmaxf(m_run[nt], m * a.scale_log2);
         const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - mn);   // 0 on the first tile
         m_run[nt] = mn;
+        thr[nt] = (mn + kLazyLog2) * inv_scale_log2;
         ol[nt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[nt][dt] *= alpha;
@@ -426,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const h8 va = *reinterpret_cast<const h8*>(&vt[(dt * 16 + c16) * VP + kk * 32 + 8 * g]);
+        const h8 va = *reinterpret_cast<const h8*>(&vt[(dt * 16 + c16) * VP + kk * 32 + 8 * (g ^ ((c16 >> 1) & 1))]);
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt)
           o[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[nt][kk], o[nt][dt], 0, 0, 0);
