@@ -63,7 +63,7 @@ CSRC = os.path.join(ROOT, "bit_kv_cache_int2_amd", "csrc")
 APPEND_COUNTERS = (os.path.join(ROOT, "profiles", "tile_append_llm_decode_counters.txt"),
                    [os.path.join(CSRC, f) for f in ("quantize.hip", "device.h")])
 DECODE_COUNTERS = (os.path.join(ROOT, "profiles", "decode_mfma_llm_decode_counters.txt"),
-                   [os.path.join(CSRC, f) for f in ("decode.hip", "device.h")])
+                   [os.path.join(CSRC, f) for f in ("decode.hip", "code_operand.h", "device.h")])
 
 
 def _source_hash(paths) -> str:
