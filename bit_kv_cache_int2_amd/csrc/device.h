@@ -46,13 +46,15 @@ KVQ_DEV uint4 ld_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Unpack 8 bf16 held in a uint4 into fp32, canonicalising -0 to +0.
+// Unpack 8 bf16 held in a uint4 into fp32 (exact; a -0 stays -0: the
+// quantizers canonicalise the group minimum and maximum instead, which is
+// all a zero's sign can reach, since comparisons treat the two zeros alike).
 KVQ_DEV void bf16x8_to_f32(const uint4 u, float* x) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    x[2 * i] = __uint_as_float(w[i] << 16) + 0.0f;
-    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u) + 0.0f;
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
   }
 }
 
@@ -64,8 +66,12 @@ struct Q2 {
   uint32_t word;  // fp16 scale bits | fp16 zero bits << 16
 };
 
+// Group parameters from the group's minimum and maximum (canonicalised
+// here, so inputs may carry either zero sign).
 KVQ_DEV Q2 q2_make(float mn, float mx) {
   Q2 q;
+  mn = mn + 0.0f;
+  mx = mx + 0.0f;
   const float s32 = (mx - mn) / 3.0f;
   const uint32_t sh = f32_to_f16_bits(s32), zh = f32_to_f16_bits(mn);
   q.s = f16_bits_to_f32(sh);
@@ -78,8 +84,11 @@ KVQ_DEV Q2 q2_make(float mn, float mx) {
   return q;
 }
 
+// Number of thresholds at or below x.  The thresholds are ordered (s >= 0),
+// so the middle one picks which of the outer two decides the low bit.
 KVQ_DEV uint32_t q2_code(float x, const Q2& q) {
-  return (uint32_t)(x >= q.t0) + (uint32_t)(x >= q.t1) + (uint32_t)(x >= q.t2);
+  const bool up = x >= q.t1;
+  return (up ? 2u : 0u) + (uint32_t)(x >= (up ? q.t2 : q.t0));
 }
 
 // Wave-level reductions (64 lanes) with butterfly shuffles.

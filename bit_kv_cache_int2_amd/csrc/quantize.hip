@@ -24,7 +24,7 @@ namespace {
 // elements per lane, element index = lane-in-row * 8 + k).  Stages run with
 // h = 1, 2, 4 in-lane and then h = 8, 16, ... across lanes, each pair (i,
 // i+h) becoming (a+b, a-b); finally every element is scaled by
-// fp32(1/sqrt(D)) and canonicalised.
+// fp32(1/sqrt(D)).
 template <int D>
 KVQ_DEV void wht_row(float (&x)[8]) {
 #pragma unroll
@@ -50,7 +50,7 @@ KVQ_DEV void wht_row(float (&x)[8]) {
   }
   const float c = __uint_as_float(D == 128 ? 0x3DB504F3u : 0x3E000000u);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) x[k] = x[k] * c + 0.0f;
+  for (int k = 0; k < 8; ++k) x[k] = x[k] * c;
 }
 
 // ---------------------------------------------------------------- append
@@ -235,7 +235,8 @@ __global__ __launch_bounds__(256) void tile_append_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float x = kx[k][e];
-        bits |= ((uint32_t)(x >= t0[e]) + (uint32_t)(x >= t1[e]) + (uint32_t)(x >= t2[e])) << (2 * e);
+        const bool up = x >= t1[e];   // ordered thresholds: see q2_code
+        bits |= ((up ? 2u : 0u) + (uint32_t)(x >= (up ? t2[e] : t0[e]))) << (2 * e);
       }
       *reinterpret_cast<uint16_t*>(kcodes + (bh * Tcap + wb + r0 + RPP * k) * (D / 4) + j * 2) =
           (uint16_t)bits;
