@@ -111,6 +111,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, c16 = lane & 15;
   const int row0 = rb * kBM + wave * kNT * 16;
+  const bool live = row0 < a.Lq;   // wave-uniform
   const int n = a.n_tokens;
   const int n_tiles = (n + 63) / 64, n_full = n / 64;
   const int tile_begin = split * a.tiles_per_split;
@@ -349,6 +350,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
             make_uint2(pk_rne(vv[4 * gg], vv[4 * gg + 1]), pk_rne(vv[4 * gg + 2], vv[4 * gg + 3]));
     }
     __syncthreads();
+    if (!live) return;   // every row of this wave is past the end: dequantise only
 
     // ---- S^T = Khat Q^T
     f4 s[kNT][4];
