@@ -101,8 +101,9 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
   __shared__ __align__(16) _Float16 klo[LO ? 64 * KP : 8];
   __shared__ __align__(16) _Float16 vt[D * VP];
   __shared__ __align__(16) _Float16 coef[R > 0 ? 64 * 16 : 8];
-  __shared__ __align__(16) uint32_t kpar[KM == 0 ? D : 64 * NG];   // window: per channel; else per token group
-  __shared__ __align__(16) uint32_t vpar[NG][64];                   // [group][token]
+  // parameters, two sets: tile j's in set j & 1, stored one tile ahead
+  __shared__ __align__(16) uint32_t kpar[2][KM == 0 ? D : 64 * NG];   // window: per channel; else per token group
+  __shared__ __align__(16) uint32_t vpar[2][NG][64];                   // [group][token]
 
   const int rb = blockIdx.x % a.n_rb, split = blockIdx.x / a.n_rb;
   const int hq = blockIdx.y, b = blockIdx.z;
@@ -234,10 +235,20 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
     }
   };
 
+  auto store_params = [&](int tile, const Pre& f) {
+    const int ps = tile & 1;
+    if (tid < 64 * NG) vpar[ps][tid % NG][tid / NG] = f.vp;
+    if (KM == 0) {
+      if (tid < D) kpar[ps][tid] = f.kp;
+    } else {
+      if (tid < 64 * NG) kpar[ps][tid] = f.kp;
+    }
+  };
   Pre pre;
   if (tile_begin < tile_end) {
     prefetch(tile_begin, pre);
     prefetch_cent(pre);
+    store_params(tile_begin, pre);
   }
 
   // One 64-token tile; the ragged last tile (masking, key tail) is a
@@ -246,20 +257,15 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
     const int t0 = tile * 64;
     constexpr bool last = decltype(ragged)::value;    // the ragged last tile
     const bool full_keys = KM != 0 || !last;          // window keys: tail window
-    __syncthreads();  // the previous tile's LDS tiles are consumed
-    // ---- parameters -> LDS
-    if (tid < 64 * NG) vpar[tid % NG][tid / NG] = pre.vp;
-    if (KM == 0) {
-      if (tid < D) kpar[tid] = pre.kp;
-    } else {
-      if (tid < 64 * NG) kpar[tid] = pre.kp;
-    }
+    // the previous tile's LDS tiles are consumed and this tile's parameters
+    // (stored during the previous tile) are visible
+    __syncthreads();
+    const int ps = tile & 1;
     if (R > 0 && tid < 64 * 8) reinterpret_cast<uint32_t*>(coef)[(tid >> 3) * 8 + (tid & 7)] = pre.cf;
     const uint32_t kcw = pre.kcw, vcw = pre.vcw;
     float cv[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) cv[c] = pre.cv[c];
-    __syncthreads();
     // ---- the next tile's packed data is in flight during this tile
     if (tile + 1 < tile_end) prefetch(tile + 1, pre);
 
@@ -272,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
         if (KM == 0) {
           uint4 pw[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) pw[j] = *reinterpret_cast<const uint4*>(&kpar[16 * kw + 4 * j]);
+          for (int j = 0; j < 4; ++j) pw[j] = *reinterpret_cast<const uint4*>(&kpar[ps][16 * kw + 4 * j]);
           const uint32_t pv[16] = {pw[0].x, pw[0].y, pw[0].z, pw[0].w, pw[1].x, pw[1].y, pw[1].z, pw[1].w,
                                    pw[2].x, pw[2].y, pw[2].z, pw[2].w, pw[3].x, pw[3].y, pw[3].z, pw[3].w};
 #pragma unroll
@@ -281,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
             kv[c] = fma_code(cw[c & 7], c >= 8, s, __builtin_fmaf(-code_base(c & 7), s, z));
           }
         } else {
-          const uint32_t pw = kpar[tk * NG + kw / 2];
+          const uint32_t pw = kpar[ps][tk * NG + kw / 2];
           const float s = f16_bits_to_f32(pw), z = f16_bits_to_f32(pw >> 16);
           const float z16 = __builtin_fmaf(-16.0f, s, z), z4 = __builtin_fmaf(-4.0f, s, z),
                       z64 = __builtin_fmaf(-64.0f, s, z);
@@ -329,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
     if (has_v) {
       uint32_t cw[8];
       code_word(vcw, kor, cw);
-      const uint4* pr = reinterpret_cast<const uint4*>(&vpar[vc / kGroup][16 * vq]);
+      const uint4* pr = reinterpret_cast<const uint4*>(&vpar[ps][vc / kGroup][16 * vq]);
       const uint4 p4[4] = {pr[0], pr[1], pr[2], pr[3]};
       const uint32_t pv[16] = {p4[0].x, p4[0].y, p4[0].z, p4[0].w, p4[1].x, p4[1].y, p4[1].z, p4[1].w,
                                p4[2].x, p4[2].y, p4[2].z, p4[2].w, p4[3].x, p4[3].y, p4[3].z, p4[3].w};
@@ -349,6 +355,9 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
         *reinterpret_cast<uint2*>(dst + 8 * (gg ^ vs)) =
             make_uint2(pk_rne(vv[4 * gg], vv[4 * gg + 1]), pk_rne(vv[4 * gg + 2], vv[4 * gg + 3]));
     }
+    // the next tile's parameters into the other set (its last reader, the
+    // previous tile's dequantisation, finished before this tile began)
+    if (tile + 1 < tile_end) store_params(tile + 1, pre);
     __syncthreads();
     if (!live) return;   // every row of this wave is past the end: dequantise only
 
