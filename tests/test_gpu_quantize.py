@@ -94,6 +94,75 @@ def test_cluster_assign_plain_and_qsac():
     assert got[5] == 17
 
 
+def _assign_check(keys_bits, cent, w=None, topk=1, tag=""):
+    """kv_cluster_assign on the GPU equals the oracle's rule key by key."""
+    kt = dev_bf16(np.ascontiguousarray(keys_bits))
+    ct = torch.from_numpy(np.ascontiguousarray(cent, np.float32)).cuda()
+    wt = None if w is None else torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda()
+    got = kv.kv_cluster_assign(kt, ct, wt, topk=topk).cpu().numpy()
+    kf = synth.bf16_bits_to_f32(keys_bits)
+    if w is None:
+        want = np.array([oracle.assign_plain(kf[i], cent) for i in range(len(kf))])
+    else:
+        want = np.array([oracle.assign_qsac(kf[i], cent, w, topk) for i in range(len(kf))])
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{tag}: {bad.size} keys differ, first {bad[:5]} got {got[bad[:5]]} want {want[bad[:5]]}"
+    return got
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_cluster_assign_near_ties(D):
+    """Keys on the bisector of two centroids (up to bf16 rounding) and tiny
+    offsets from it: the MFMA shortlist must keep both and the rule decide."""
+    rng = np.random.default_rng(11)
+    C = 96
+    cent = rng.standard_normal((C, D)).astype(np.float32)
+    a, b = rng.integers(0, C, 400), rng.integers(0, C, 400)
+    mid = 0.5 * (cent[a] + cent[b])
+    keys = np.concatenate([mid, mid + 1e-3 * rng.standard_normal(mid.shape),
+                           mid + 1e-6 * rng.standard_normal(mid.shape)])
+    _assign_check(synth.to_bf16_bits(keys.astype(np.float32)), cent, tag=f"near ties D={D}")
+    w = rng.uniform(0.0, 2.0, D).astype(np.float32)
+    w[:5] = 0.0
+    _assign_check(synth.to_bf16_bits(keys.astype(np.float32)), cent, w, 4, tag=f"near ties qsac D={D}")
+
+
+@pytest.mark.parametrize("scale", [1e-3, 1.0, 3e3])
+def test_cluster_assign_scales_and_shapes(scale):
+    """Magnitudes far from 1, centroid counts that leave partial chunks and
+    tiles, key counts that leave partial waves and blocks."""
+    rng = np.random.default_rng(12)
+    D = 128
+    for C, n in ((1, 5), (3, 65), (70, 257), (256, 300)):
+        cent = (scale * rng.standard_normal((C, D))).astype(np.float32)
+        keys = cent[rng.integers(0, C, n)] + 0.5 * scale * rng.standard_normal((n, D))
+        kb = synth.to_bf16_bits(keys.astype(np.float32))
+        _assign_check(kb, cent, tag=f"scale={scale} C={C} n={n}")
+        w = rng.uniform(0.1, 3.0, D).astype(np.float32)
+        for topk in (1, 4):
+            if topk <= C:
+                _assign_check(kb, cent, w, topk, tag=f"qsac scale={scale} C={C} n={n} topk={topk}")
+
+
+def test_cluster_assign_exact_scan_paths():
+    """All-equal centroids (every centroid ties: the rescoring queue and the
+    QSAC lists overflow), topk above 4 and a negative weight all take the
+    exact scan; results must still follow the rule."""
+    rng = np.random.default_rng(13)
+    D, n = 128, 200
+    same = np.tile(rng.standard_normal((1, D)).astype(np.float32), (40, 1))
+    keys = synth.to_bf16_bits((rng.standard_normal((n, D))).astype(np.float32))
+    got = _assign_check(keys, same, tag="all equal")
+    assert np.all(got == 0)
+    w = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    _assign_check(keys, same, w, 4, tag="all equal qsac")
+    cent = rng.standard_normal((64, D)).astype(np.float32)
+    _assign_check(keys, cent, w, 8, tag="topk 8")
+    wn = w.copy()
+    wn[3] = -0.25
+    _assign_check(keys, cent, wn, 4, tag="negative weight")
+
+
 @pytest.mark.slow
 def test_llm_decode_build_full_size_sampled():
     """Full 16 x 32768 x 8-head window-key build (the benchmark's launch
