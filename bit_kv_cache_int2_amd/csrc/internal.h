@@ -13,6 +13,10 @@ hipError_t launch_quantize_append(const kvq_cache* c, const void* k_bf16,
                                   const void* v_bf16, int cur_len, int n_new,
                                   hipStream_t stream);
 
+// Key side of quantize-append for centroid keys (after the values).
+hipError_t launch_centroid_append(const kvq_cache* c, const void* k_bf16, int cur_len,
+                                  int n_new, hipStream_t stream);
+
 hipError_t launch_cluster_assign(const void* keys, int64_t n, int head_dim,
                                  int64_t key_stride, const float* centroids,
                                  int n_centroids, const float* sens_w, int topk,

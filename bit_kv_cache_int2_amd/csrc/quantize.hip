@@ -1,4 +1,4 @@
-// Quantise-append into the packed INT2 cache, and centroid assignment.
+// Quantise-append into the packed INT2 cache.
 //
 //  * values ([OKV] rotated values, optional) and window keys ([OKV]
 //    per-window key ranges): one block per (head, 64-token tile, sequence),
@@ -7,12 +7,7 @@
 //    quad and its min/max two xor-shuffles; the Walsh-Hadamard rotation runs
 //    in registers (three in-lane butterfly stages, then one xor-shuffle
 //    stage per remaining bit).
-//  * centroid keys ([QWM] 1): one lane per token keeps its key in registers
-//    and scans centroids staged 64 at a time in LDS (broadcast reads), in
-//    index order with the channel-order fp32 distance; QSAC keeps the best
-//    candidates in a sorted register list and scores each candidate's INT2
-//    residual; PSAC coefficients accumulate in channel order as the chosen
-//    residual is quantised.
+//  * centroid keys ([QWM] 1): the values here, the keys in assign.hip.
 #include "device.h"
 #include "internal.h"
 
@@ -256,467 +251,6 @@ __global__ __launch_bounds__(256) void tile_append_kernel(
   }
 }
 
-// ---------------------------------------------------------------- centroids
-
-// INT2-quantise the residual r = k - c per group of 32 (inputs
-// canonicalised), returning the weighted squared error of the dequantised
-// residual (fp32, channel order; 0 when w == nullptr).  Optionally emits the
-// packed codes, the parameter words and the PSAC accumulators.
-template <int D, int R, bool EMIT>
-KVQ_DEV float residual_q2(const float (&k)[D], const float* __restrict__ c,
-                          const float* w, const float* U, uint32_t* codes,
-                          uint32_t* prm, float* pacc) {
-  float E = 0.0f;
-#pragma unroll
-  for (int g = 0; g < D / kGroup; ++g) {
-    float r[kGroup];
-#pragma unroll
-    for (int i = 0; i < kGroup; i += 4) {
-      const float4 c4 = *reinterpret_cast<const float4*>(c + g * kGroup + i);
-      r[i] = (k[g * kGroup + i] - c4.x) + 0.0f;
-      r[i + 1] = (k[g * kGroup + i + 1] - c4.y) + 0.0f;
-      r[i + 2] = (k[g * kGroup + i + 2] - c4.z) + 0.0f;
-      r[i + 3] = (k[g * kGroup + i + 3] - c4.w) + 0.0f;
-    }
-    float mn = r[0], mx = r[0];
-#pragma unroll
-    for (int i = 1; i < kGroup; ++i) {
-      mn = fminf(mn, r[i]);
-      mx = fmaxf(mx, r[i]);
-    }
-    const Q2 q = q2_make(mn, mx);
-    if (EMIT) prm[g] = q.word;
-    uint32_t wlo = 0, whi = 0;
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      const uint32_t code = q2_code(r[i], q);
-      if (i < 16) wlo |= code << (2 * i);
-      else whi |= code << (2 * (i - 16));
-      const float e = r[i] - __builtin_fmaf((float)code, q.s, q.z);
-      const int d = g * kGroup + i;
-      if (w != nullptr) {
-        const float we = w[d] * e;
-        E = __builtin_fmaf(we, e, E);
-      }
-      if (EMIT && R > 0) {
-#pragma unroll
-        for (int m = 0; m < R; ++m) pacc[m] = __builtin_fmaf(U[d * R + m], e, pacc[m]);
-      }
-    }
-    if (EMIT) {
-      codes[2 * g] = wlo;
-      codes[2 * g + 1] = whi;
-    }
-  }
-  return E;
-}
-
-// Exact squared distance of key row kr (bf16) to centroid row cr (fp32): the
-// fp32 sum in channel order with fma, t = k - c; QSAC weighs each term as
-// fma(w t, t) with w t rounded first.
-template <int D, bool QSAC>
-KVQ_DEV float exact_dist(const uint16_t* __restrict__ kr, const float* __restrict__ cr, const float* w) {
-  float acc = 0.0f;
-#pragma unroll 4
-  for (int d = 0; d < D; d += 8) {
-    float x[8];
-    bf16x8_to_f32(*reinterpret_cast<const uint4*>(kr + d), x);
-    const float4 c0 = *reinterpret_cast<const float4*>(cr + d), c1 = *reinterpret_cast<const float4*>(cr + d + 4);
-    const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float t = x[u] - cc[u];
-      acc = QSAC ? __builtin_fmaf(w[d + u] * t, t, acc) : __builtin_fmaf(t, t, acc);
-    }
-  }
-  return acc;
-}
-
-// Distance (bits, non-negative) and index packed so that the u64 order is
-// the lexicographic order (distance, index) of the assignment rules.
-KVQ_DEV unsigned long long dist_key(float dist, int j) {
-  return ((unsigned long long)__float_as_uint(dist) << 32) | (uint32_t)j;
-}
-
-typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-
-// Centroid assignment with the exact result and most of the work on MFMA.
-//
-// Block = 4 waves x 64 keys.  The centroid table streams through LDS 64 rows
-// at a time, split into bf16 hi + lo parts (c ~ hi + lo within 2^-18 |c|;
-// QSAC uses the rows w*c).  Per wave, bf16 MFMAs give every (key,
-// centroid) pair  d~ = |c|^2 - 2 k.c  (the key's |k|^2 is common to all
-// centroids and left out), whose distance to the exact fp32 distance of
-// the assignment rule (less |k|^2) is below 2^-13 (|k| + |c|)^2 (MFMA
-// accumulation, the hi/lo split, the fp32 rounding of the rule itself; the
-// norms are weighted for QSAC).  With the margin M = 2^-11 (|k|^2 + |c|^2) +
-// 1e-30, at least twice that, each pair has an interval [d~ - M, d~ + M]
-// around its exact value.
-// A key keeps U = the smallest upper end seen so far (QSAC: at most the
-// 4th smallest, merged from the four lanes that share the key), and every
-// centroid whose lower end is at most U is rescored exactly; the winner
-// (QSAC: each of the top-4) has its lower end below the final U, so it is
-// always rescored, and the rescored set decides with the rule's own
-// arithmetic and tie order.  Rescoring goes through a per-wave queue in LDS
-// that all 64 lanes drain once the table has been seen; the best (distance, index) per key is kept by a
-// 64-bit LDS atomic min (QSAC: a list per key).  A key whose queue or list
-// overflows, weights that are negative or not finite, or topk > 4 fall back
-// to the exact scan of every centroid, lane per key.  Then, lane per key:
-// QSAC scores its top-k candidates by the INT2 residual error, and
-// TO_CACHE writes idx/codes/params/PSAC into the cache rows at cur_len + i
-// (otherwise the i32 index goes to idx_out).
-constexpr int kCandMax = 8;    // QSAC candidates (topk <= kCandMax)
-constexpr int kCChunk = 64;    // centroids per LDS chunk
-constexpr int kQueue = 1024;   // per-wave rescoring queue
-constexpr int kList = 16;      // QSAC: exactly scored candidates kept per key
-constexpr float kMarginRel = 1.0f / 4096.0f;
-constexpr float kMarginAbs = 1e-30f;
-
-template <int D, bool QSAC, int R, bool TO_CACHE>
-__global__ __launch_bounds__(256) void centroid_kernel(
-    const uint16_t* __restrict__ kin, int64_t key_stride, int64_t head_stride,
-    int64_t batch_stride, int64_t n, const float* __restrict__ cent, int C,
-    const float* __restrict__ sens_w, int topk, const float* __restrict__ basis,
-    int32_t* __restrict__ idx_out, uint8_t* __restrict__ kidx,
-    uint8_t* __restrict__ kcodes, uint32_t* __restrict__ kparams,
-    uint16_t* __restrict__ kpsac, int H, int Tcap, int cur_len) {
-  constexpr int NKS = D / 32;
-  constexpr int CP = D + 16;   // chunk row pitch (bf16): conflict-free operand reads
-  __shared__ __align__(16) __bf16 chi[kCChunk * CP];
-  __shared__ __align__(16) __bf16 clo[kCChunk * CP];
-  __shared__ __align__(16) float cup[kCChunk], clo_[kCChunk];   // |c|^2 + Mc, |c|^2 - Mc
-  __shared__ float wl[D];
-  __shared__ float ul[D * (R > 0 ? R : 1)];
-  __shared__ uint32_t queue[4][kQueue];
-  __shared__ int qcount[4];
-  __shared__ unsigned long long best[QSAC ? 1 : 256];
-  __shared__ unsigned long long clist[QSAC ? 256 * kList : 1];
-  __shared__ int ccount[QSAC ? 256 : 1];
-  __shared__ int bad_w;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, c16 = lane & 15;
-  const int64_t bh = (int64_t)blockIdx.z * H + blockIdx.y;
-  const int64_t kbase = (int64_t)blockIdx.x * 256 + wave * 64;   // this wave's 64 keys
-  const float* cb = cent + bh * (int64_t)C * D;
-  const uint16_t* kb = kin + blockIdx.z * batch_stride + blockIdx.y * head_stride;
-
-  if (QSAC)
-    for (int d = tid; d < D; d += 256) wl[d] = sens_w[bh * D + d];
-  if (R > 0)
-    for (int d = tid; d < D * R; d += 256) ul[d] = basis[bh * D * R + d];
-  if (tid == 0) bad_w = 0;
-  if (QSAC) ccount[tid] = 0;
-  else best[tid] = ~0ull;
-  if (lane == 0) qcount[wave] = 0;
-  __syncthreads();
-  if (QSAC && tid < D && !(wl[tid] >= 0.0f && wl[tid] < __builtin_inff())) bad_w = 1;
-  __syncthreads();
-  const bool exact_scan = (QSAC && (bad_w != 0 || topk > 4));
-
-  // ---- this wave's keys as the B operand (bf16 is exact); lane (g, c16)
-  // holds dims 32 ks + 8 g .. + 7 of key 16 nt + c16
-  bf8 kop[4][NKS];
-  float mk[4];     // Mk = 2^-11 |k|^2 + 1e-30 (|k| weighted for QSAC)
-  bool kok[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int64_t i = kbase + nt * 16 + c16;
-    kok[nt] = i < n;
-    float s2 = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const uint4 u = kok[nt] ? *reinterpret_cast<const uint4*>(kb + i * key_stride + ks * 32 + 8 * g)
-                              : make_uint4(0u, 0u, 0u, 0u);
-      kop[nt][ks] = __builtin_bit_cast(bf8, u);
-      float x[8];
-      bf16x8_to_f32(u, x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s2 = __builtin_fmaf(QSAC ? wl[ks * 32 + 8 * g + e] * x[e] : x[e], x[e], s2);
-    }
-    s2 += __shfl_xor(s2, 16, 64);
-    s2 += __shfl_xor(s2, 32, 64);
-    mk[nt] = __builtin_fmaf(2.0f * kMarginRel, s2, kMarginAbs);   // the key's part of the margin
-  }
-  // U (plain) or this lane's four smallest upper ends (QSAC), per key slot
-  float U[4], t4[4][4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    U[nt] = __builtin_inff();
-#pragma unroll
-    for (int r = 0; r < 4; ++r) t4[nt][r] = __builtin_inff();
-  }
-
-  for (int c0 = 0; c0 < C && !exact_scan; c0 += kCChunk) {
-    __syncthreads();   // the previous chunk is consumed
-    {
-      // thread -> row tid / 4, a quarter of its channels
-      const int r = tid >> 2, q = tid & 3, j = c0 + r;
-      float s2 = 0.0f;
-#pragma unroll
-      for (int d = q * (D / 4); d < (q + 1) * (D / 4); d += 4) {
-        const float4 v = (j < C) ? *reinterpret_cast<const float4*>(cb + (int64_t)j * D + d)
-                                 : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        const float x[4] = {v.x, v.y, v.z, v.w};
-        __bf16 hv[4], lv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float y = QSAC ? wl[d + e] * x[e] : x[e];
-          s2 = __builtin_fmaf(y, x[e], s2);
-          hv[e] = (__bf16)y;
-          lv[e] = (__bf16)(y - (float)hv[e]);
-        }
-        typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
-        *reinterpret_cast<bf4*>(&chi[r * CP + d]) = bf4{hv[0], hv[1], hv[2], hv[3]};
-        *reinterpret_cast<bf4*>(&clo[r * CP + d]) = bf4{lv[0], lv[1], lv[2], lv[3]};
-      }
-      s2 += __shfl_xor(s2, 1, 64);
-      s2 += __shfl_xor(s2, 2, 64);
-      if (q == 0) {
-        // s2 = |c|^2 (sum w c^2 for QSAC); the centroid's part of the margin
-        // is Mc = 2^-11 |c|^2; rows past the table never qualify
-        const float mc = 2.0f * kMarginRel * s2;
-        cup[r] = (j < C) ? s2 + mc : __builtin_inff();
-        clo_[r] = (j < C) ? s2 - mc : __builtin_inff();
-      }
-    }
-    __syncthreads();
-
-    // ---- S = C_chunk K^T: row = centroid 16 mt + 4 g + i, column = key 16 nt + c16
-    f4 acc[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int off = (mt * 16 + c16) * CP + ks * 32 + 8 * g;
-        const bf8 ah = *reinterpret_cast<const bf8*>(&chi[off]);
-        const bf8 al = *reinterpret_cast<const bf8*>(&clo[off]);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, kop[nt][ks], acc[mt][nt], 0, 0, 0);
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, kop[nt][ks], acc[mt][nt], 0, 0, 0);
-        }
-      }
-
-    // ---- intervals, U, candidates.  With M = Mk + Mc >= 2^-12 (|k| + |c|)^2
-    // (as (a + b)^2 <= 2 a^2 + 2 b^2) the ends are
-    //   upper = (|c|^2 + Mc - 2 k.c) + Mk,  lower = (|c|^2 - Mc - 2 k.c) - Mk,
-    // so U = min upper = min(vu) + Mk and lower <= U  <=>  vl <= min(vu) + 2 Mk.
-    float cuv[4][4], clv[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const float4 au = *reinterpret_cast<const float4*>(&cup[mt * 16 + 4 * g]);
-      const float4 al = *reinterpret_cast<const float4*>(&clo_[mt * 16 + 4 * g]);
-      cuv[mt][0] = au.x; cuv[mt][1] = au.y; cuv[mt][2] = au.z; cuv[mt][3] = au.w;
-      clv[mt][0] = al.x; clv[mt][1] = al.y; clv[mt][2] = al.z; clv[mt][3] = al.w;
-    }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      float vl[4][4];
-      float um = __builtin_inff();
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float vu = __builtin_fmaf(-2.0f, acc[mt][nt][i], cuv[mt][i]);
-          vl[mt][i] = __builtin_fmaf(-2.0f, acc[mt][nt][i], clv[mt][i]);
-          if (QSAC) {
-            // keep this lane's four smallest (upper ends less Mk)
-            float v = vu;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float a0 = t4[nt][r];
-              t4[nt][r] = fminf(a0, v);
-              v = fmaxf(a0, v);
-            }
-          } else {
-            um = fminf(um, vu);
-          }
-        }
-      float uu;
-      if (QSAC) {
-        // 4th smallest over the four lanes of the key (disjoint centroid
-        // sets): two bitonic merges of sorted 4-lists
-        float m[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) m[r] = fminf(t4[nt][r], __shfl_xor(t4[nt][3 - r], 16, 64));
-        const float a0 = fminf(m[0], m[2]), a2 = fmaxf(m[0], m[2]), a1 = fminf(m[1], m[3]), a3 = fmaxf(m[1], m[3]);
-        const float srt[4] = {fminf(a0, a1), fmaxf(a0, a1), fminf(a2, a3), fmaxf(a2, a3)};
-        float top = -__builtin_inff();
-#pragma unroll
-        for (int r = 0; r < 4; ++r) top = fmaxf(top, fminf(srt[r], __shfl_xor(srt[3 - r], 32, 64)));
-        uu = top;
-      } else {
-        uu = um;
-        uu = fminf(uu, __shfl_xor(uu, 16, 64));
-        uu = fminf(uu, __shfl_xor(uu, 32, 64));
-      }
-      U[nt] = fminf(U[nt], uu);
-      const float thr = U[nt] + 2.0f * mk[nt];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // a NaN bound counts as a candidate; rows past the table are +inf
-          if (kok[nt] && !(vl[mt][i] > thr)) {
-            const int j = c0 + mt * 16 + 4 * g + i;
-            const int pos = atomicAdd(&qcount[wave], 1);
-            if (pos < kQueue) queue[wave][pos] = ((uint32_t)(nt * 16 + c16) << 16) | (uint32_t)j;
-          }
-        }
-    }
-  }
-
-  // ---- drain the queue once: exact distances, lanes in parallel
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-  const int cnt = __builtin_amdgcn_readfirstlane(qcount[wave]);
-  const bool overflow = cnt > kQueue;   // wave-uniform
-  if (!overflow && !exact_scan) {
-    for (int e = lane; e < cnt; e += 64) {
-      const uint32_t ent = queue[wave][e];
-      const int kl = (int)(ent >> 16), j = (int)(ent & 0xFFFFu);
-      if (j >= C) continue;   // only when every bound was infinite
-      const float dist = exact_dist<D, QSAC>(kb + (kbase + kl) * key_stride, cb + (int64_t)j * D, wl);
-      if (QSAC) {
-        const int pos = atomicAdd(&ccount[wave * 64 + kl], 1);
-        if (pos < kList) clist[(wave * 64 + kl) * kList + pos] = dist_key(dist, j);
-      } else {
-        atomicMin(&best[wave * 64 + kl], dist_key(dist, j));
-      }
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-
-  // ---- lane per key
-  const int64_t i = kbase + lane;
-  const bool ok = i < n;
-  if (!ok) return;
-  const uint16_t* kr = kb + i * key_stride;
-  float k[D];
-#pragma unroll
-  for (int j = 0; j < D / 8; ++j) {
-    float x[8];
-    bf16x8_to_f32(*reinterpret_cast<const uint4*>(kr + j * 8), x);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) k[j * 8 + t] = x[t];
-  }
-  int bestj = 0;
-  int cj[kCandMax];
-#pragma unroll
-  for (int t = 0; t < kCandMax; ++t) cj[t] = 0;
-  bool scan = exact_scan || overflow;
-  if (QSAC && !scan) {
-    const int m = ccount[wave * 64 + lane];
-    if (m > kList) {
-      scan = true;
-    } else {
-      // the top-k of the scored list in (distance, index) order
-      unsigned long long prev = 0ull;
-      bool first = true;
-#pragma unroll
-      for (int t = 0; t < kCandMax; ++t) {
-        if (t < topk && t < C) {
-          unsigned long long mv = ~0ull;
-          for (int e = 0; e < m; ++e) {
-            const unsigned long long v = clist[(wave * 64 + lane) * kList + e];
-            if ((first || v > prev) && v < mv) mv = v;
-          }
-          cj[t] = (int)(mv & 0xFFFFFFFFull);
-          prev = mv;
-          first = false;
-        }
-      }
-    }
-  } else if (!QSAC && !scan) {
-    bestj = (int)(best[wave * 64 + lane] & 0xFFFFFFFFull);
-  }
-  if (scan) {
-    // every centroid, in index order, with the rule's arithmetic
-    float bd = __builtin_inff();
-    float cd[kCandMax];
-#pragma unroll
-    for (int t = 0; t < kCandMax; ++t) {
-      cd[t] = __builtin_inff();
-      cj[t] = 0;
-    }
-    for (int j = 0; j < C; ++j) {
-      const float dist = exact_dist<D, QSAC>(kr, cb + (int64_t)j * D, wl);
-      if (QSAC) {
-        float vd = dist;
-        int vj = j;
-#pragma unroll
-        for (int t = 0; t < kCandMax; ++t) {
-          if (vd < cd[t]) {
-            const float td = cd[t];
-            const int tj = cj[t];
-            cd[t] = vd;
-            cj[t] = vj;
-            vd = td;
-            vj = tj;
-          }
-        }
-      } else if (dist < bd) {
-        bd = dist;
-        bestj = j;
-      }
-    }
-  }
-  if (QSAC) {
-    float bE = 0.0f;
-    bestj = -1;
-#pragma unroll
-    for (int t = 0; t < kCandMax; ++t) {
-      if (t < topk && t < C) {
-        const int j = cj[t];
-        const float E = residual_q2<D, 0, false>(k, cb + (int64_t)j * D, wl, nullptr,
-                                                 nullptr, nullptr, nullptr);
-        if (bestj < 0 || E < bE || (E == bE && j < bestj)) {
-          bestj = j;
-          bE = E;
-        }
-      }
-    }
-  }
-  if (!TO_CACHE) {
-    idx_out[i] = bestj;
-    return;
-  }
-  uint32_t codes[D / 16];
-  uint32_t prm[D / kGroup];
-  float pacc[R > 0 ? R : 1];
-#pragma unroll
-  for (int m = 0; m < (R > 0 ? R : 1); ++m) pacc[m] = 0.0f;
-  residual_q2<D, R, true>(k, cb + (int64_t)bestj * D, nullptr, ul, codes, prm, pacc);
-  const int64_t orow = bh * Tcap + cur_len + i;
-  kidx[orow] = (uint8_t)bestj;
-  uint4* cdst = reinterpret_cast<uint4*>(kcodes + orow * (D / 4));
-#pragma unroll
-  for (int q = 0; q < D / 64; ++q)
-    cdst[q] = make_uint4(codes[4 * q], codes[4 * q + 1], codes[4 * q + 2], codes[4 * q + 3]);
-  uint32_t* pdst = kparams + orow * (D / kGroup);
-#pragma unroll
-  for (int gq = 0; gq < D / kGroup; ++gq) pdst[gq] = prm[gq];
-  if (R > 0) {
-    uint32_t hw[(R > 0 ? R : 2) / 2];
-#pragma unroll
-    for (int m = 0; m < R; m += 2)
-      hw[m / 2] = f32_to_f16_bits(pacc[m]) | (f32_to_f16_bits(pacc[m + 1]) << 16);
-    uint32_t* ps = reinterpret_cast<uint32_t*>(kpsac + orow * (R > 0 ? R : 1));
-#pragma unroll
-    for (int m = 0; m < R / 2; ++m) ps[m] = hw[m];
-  }
-}
-
 template <int D, bool KEYS>
 hipError_t launch_tile_append(const kvq_cache* c, const void* k, const void* v, int cur_len,
                               int n_new, hipStream_t st) {
@@ -735,19 +269,6 @@ hipError_t launch_tile_append(const kvq_cache* c, const void* k, const void* v, 
   return hipGetLastError();
 }
 
-template <int D, bool QSAC, int R>
-hipError_t launch_centroid_cache(const kvq_cache* c, const void* k, int cur_len, int n_new,
-                                 hipStream_t st) {
-  const kvq_layout& L = c->layout;
-  const dim3 grid((unsigned)((n_new + 255) / 256), (unsigned)L.kv_heads, (unsigned)L.batch);
-  centroid_kernel<D, QSAC, R, true><<<grid, 256, 0, st>>>(
-      (const uint16_t*)k, (int64_t)L.kv_heads * D, D, (int64_t)n_new * L.kv_heads * D, n_new,
-      (const float*)c->centroids, L.n_centroids, (const float*)c->sens_w, L.qsac_topk,
-      (const float*)c->psac_basis, nullptr, (uint8_t*)c->k_idx, (uint8_t*)c->k_codes,
-      (uint32_t*)c->k_params, (uint16_t*)c->k_psac, L.kv_heads, L.capacity, cur_len);
-  return hipGetLastError();
-}
-
 template <int D>
 hipError_t launch_append(const kvq_cache* c, const void* k, const void* v, int cur_len,
                          int n_new, hipStream_t st) {
@@ -755,22 +276,7 @@ hipError_t launch_append(const kvq_cache* c, const void* k, const void* v, int c
   if (L.key_mode == KVQ_KEY_WINDOW) return launch_tile_append<D, true>(c, k, v, cur_len, n_new, st);
   hipError_t e = launch_tile_append<D, false>(c, k, v, cur_len, n_new, st);
   if (e != hipSuccess) return e;
-  const bool qsac = L.key_mode == KVQ_KEY_CENTROID_QSAC;
-  if (L.psac_rank == 8)
-    return qsac ? launch_centroid_cache<D, true, 8>(c, k, cur_len, n_new, st)
-                : launch_centroid_cache<D, false, 8>(c, k, cur_len, n_new, st);
-  return qsac ? launch_centroid_cache<D, true, 0>(c, k, cur_len, n_new, st)
-              : launch_centroid_cache<D, false, 0>(c, k, cur_len, n_new, st);
-}
-
-template <int D, bool QSAC>
-hipError_t launch_assign_t(const void* keys, int64_t n, int64_t stride, const float* cent,
-                           int C, const float* w, int topk, int32_t* out, hipStream_t st) {
-  const dim3 grid((unsigned)((n + 255) / 256), 1, 1);
-  centroid_kernel<D, QSAC, 0, false><<<grid, 256, 0, st>>>(
-      (const uint16_t*)keys, stride, 0, 0, n, cent, C, w, topk, nullptr, out, nullptr,
-      nullptr, nullptr, nullptr, 1, 0, 0);
-  return hipGetLastError();
+  return launch_centroid_append(c, k, cur_len, n_new, st);   // assign.hip
 }
 
 }  // namespace
@@ -781,18 +287,6 @@ hipError_t launch_quantize_append(const kvq_cache* c, const void* k_bf16,
   if (n_new == 0) return hipSuccess;
   return (c->layout.head_dim == 128) ? launch_append<128>(c, k_bf16, v_bf16, cur_len, n_new, stream)
                                      : launch_append<64>(c, k_bf16, v_bf16, cur_len, n_new, stream);
-}
-
-hipError_t launch_cluster_assign(const void* keys, int64_t n, int head_dim,
-                                 int64_t key_stride, const float* centroids,
-                                 int n_centroids, const float* sens_w, int topk,
-                                 int32_t* idx_out, hipStream_t stream) {
-  if (n == 0) return hipSuccess;
-  if (head_dim == 128)
-    return sens_w ? launch_assign_t<128, true>(keys, n, key_stride, centroids, n_centroids, sens_w, topk, idx_out, stream)
-                  : launch_assign_t<128, false>(keys, n, key_stride, centroids, n_centroids, nullptr, 1, idx_out, stream);
-  return sens_w ? launch_assign_t<64, true>(keys, n, key_stride, centroids, n_centroids, sens_w, topk, idx_out, stream)
-                : launch_assign_t<64, false>(keys, n, key_stride, centroids, n_centroids, nullptr, 1, idx_out, stream);
 }
 
 }  // namespace kvq
