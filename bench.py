@@ -238,6 +238,55 @@ def chunk_workload(name: str, steps: int, warmup: int) -> dict:
     return rec
 
 
+def kmeans_workload(steps: int, warmup: int) -> dict:
+    """Calibration: Lloyd rounds of kv_kmeans over the video workload's
+    cached keys (40 heads x 31200 keys, 256 centroids, head_dim 128); one
+    step = one round for every head, each head starting from its picks."""
+    import numpy as np
+    import torch
+
+    import bit_kv_cache_int2_amd as kv
+    import synth
+
+    d = synth.video_chunk()
+    H, T = d["Hkv"], d["T"]
+    C = 256
+    kd = torch.from_numpy(np.ascontiguousarray(d["K"]).view(np.int16)).view(torch.bfloat16).cuda()
+    K = synth.bf16_bits_to_f32(d["K"])[0]
+    D = K.shape[-1]
+    init = torch.from_numpy(np.ascontiguousarray(
+        np.stack([K[d["kmeans_init"][0, h], h] for h in range(H)]))).cuda()[None]   # [1][H][C][D]
+    cent = init.clone()
+    asg = torch.empty((1, H, T), dtype=torch.int32, device="cuda")
+    ws = torch.empty(kv.lib().kv_kmeans_workspace(1, H, T), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():    # one call: every head's round
+        cent.copy_(init)
+        kv.kv_kmeans(kd, cent, 1, assign_out=asg, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t = ev0.elapsed_time(ev1) * 1e-3 / steps
+    return {"metric": "k-means round time (all heads)", "value": round(t * 1e6, 1), "unit": "us",
+            "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": round(wall / steps * 1e3, 4), "higher_is_better": False,
+            "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+            "config": {"workload": "kmeans", "heads": H, "keys_per_head": T, "centroids": C,
+                       "head_dim": D, "rule": "exact fp32 assignment, fp64 key-order means"},
+            "kmeans": {"us_per_round": round(t * 1e6, 1),
+                       "g_key_assignments_s": round(H * T / t / 1e9, 3)}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,7 +294,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="llm_decode",
-                    choices=["llm_decode", "long_history", "video_chunk", "sensitivity", "copy"])
+                    choices=["llm_decode", "long_history", "video_chunk", "sensitivity", "kmeans", "copy"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the path has no multi-GPU leg "
@@ -256,7 +305,9 @@ def main() -> int:
     if args.workload != "llm_decode":
         import torch
         torch.cuda.set_device(0)
-        print(json.dumps(chunk_workload(args.workload, args.steps, args.warmup)), flush=True)
+        run = kmeans_workload if args.workload == "kmeans" else (
+            lambda s, w: chunk_workload(args.workload, s, w))
+        print(json.dumps(run(args.steps, args.warmup)), flush=True)
         return 0
 
     import numpy as np

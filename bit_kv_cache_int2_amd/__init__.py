@@ -72,6 +72,10 @@ def lib():
     L.kv_quantize_append.restype = ctypes.c_int
     L.kv_cluster_assign.argtypes = [vp, i64, i32, i64, vp, i32, vp, i32, vp, vp]
     L.kv_cluster_assign.restype = ctypes.c_int
+    L.kv_kmeans_workspace.argtypes = [i32, i32, i64]
+    L.kv_kmeans_workspace.restype = sz
+    L.kv_kmeans.argtypes = [vp, i32, i64, i32, i32, i64, i64, i64, vp, i32, i32, vp, vp, sz, vp]
+    L.kv_kmeans.restype = ctypes.c_int
     L.attn_int2_decode_workspace.argtypes = [pL, i32, i32]
     L.attn_int2_decode_workspace.restype = sz
     L.attn_int2_decode.argtypes = [pC, i32, vp, i32, i32, ctypes.c_float, vp, i32, vp, vp, sz, vp]
@@ -189,6 +193,37 @@ def kv_cluster_assign(keys: torch.Tensor, centroids: torch.Tensor, sens_w=None, 
                                    centroids.shape[0], _ptr(sens_w), int(topk), _ptr(out),
                                    _stream(stream)), "kv_cluster_assign")
     return out
+
+
+def kv_kmeans(keys: torch.Tensor, centroids: torch.Tensor, iters: int, assign_out=None,
+              workspace=None, stream=None):
+    """Lloyd k-means of bf16 keys [B, n, H, D] (one table per (b, h); any
+    strides with a unit last one), or of one key matrix [n, D], starting from
+    centroids f32 [B, H, C, D] (or [C, D]), which are updated in place.
+    Returns (centroids, assignment i32 [B, H, n] (or [n]) of the last round)."""
+    if keys.dtype != torch.bfloat16 or not keys.is_cuda or keys.stride(-1) != 1:
+        raise ValueError("keys must be a bf16 device tensor with unit last stride")
+    if keys.dim() == 2:
+        k4 = keys[None, :, None, :]
+        c4 = centroids[None, None]
+    elif keys.dim() == 4:
+        k4, c4 = keys, centroids
+    else:
+        raise ValueError("keys must be [n, D] or [B, n, H, D]")
+    _need_cuda(centroids, "centroids", torch.float32)
+    B, n, H, D = k4.shape
+    if tuple(c4.shape[:2]) != (B, H) or c4.shape[3] != D or not centroids.is_contiguous():
+        raise ValueError("centroids must be contiguous f32 [B, H, C, D] ([C, D] for 2-D keys)")
+    if assign_out is None:
+        assign_out = torch.empty((B, H, n) if keys.dim() == 4 else (n,), dtype=torch.int32,
+                                 device=keys.device)
+    if workspace is None:
+        workspace = torch.empty(max(int(lib().kv_kmeans_workspace(B, H, n)), 16), dtype=torch.uint8,
+                                device=keys.device)
+    _check(lib().kv_kmeans(_ptr(keys), B, n, H, D, k4.stride(1), k4.stride(2), k4.stride(0),
+                           _ptr(centroids), c4.shape[2], int(iters), _ptr(assign_out),
+                           _ptr(workspace), workspace.numel(), _stream(stream)), "kv_kmeans")
+    return centroids, assign_out
 
 
 def decode_workspace(cache: KVCache, q_heads: int, n_tokens: int, device="cuda") -> torch.Tensor:

@@ -151,6 +151,33 @@ int kv_cluster_assign(const void* keys, int64_t n, int32_t head_dim, int64_t key
                                                (hipStream_t)stream));
 }
 
+size_t kv_kmeans_workspace(int32_t batch, int32_t heads, int64_t n) {
+  if (batch < 0 || heads < 0 || n < 0 || n > ((int64_t)1 << 31) - 256) return 0;
+  return kvq::kmeans_workspace_bytes(batch, heads, n);
+}
+
+int kv_kmeans(const void* keys, int32_t batch, int64_t n, int32_t heads, int32_t head_dim,
+              int64_t key_stride, int64_t head_stride, int64_t batch_stride, float* centroids,
+              int32_t n_centroids, int32_t iters, int32_t* assign_out, void* ws, size_t ws_bytes,
+              void* stream) {
+  if (n < 0 || batch < 0 || heads < 0 || iters < 0) return KVQ_EINVAL;
+  if (head_dim != 64 && head_dim != 128) return KVQ_EUNSUPPORTED;
+  if (n_centroids < 1 || n_centroids > 256) return KVQ_EUNSUPPORTED;
+  if (n == 0 || batch == 0 || heads == 0) return KVQ_OK;
+  if (!keys || !centroids || !aligned16(keys) || !aligned16(centroids) ||
+      ((uintptr_t)assign_out & 3u))
+    return KVQ_EINVAL;
+  if (key_stride < head_dim || key_stride % 8 != 0 || head_stride < 0 || head_stride % 8 != 0 ||
+      batch_stride < 0 || batch_stride % 8 != 0)
+    return KVQ_EINVAL;
+  if (n > ((int64_t)1 << 31) - 256) return KVQ_EINVAL;
+  const size_t need = kv_kmeans_workspace(batch, heads, n);
+  if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < need) return KVQ_EWORKSPACE;
+  return hip_status(kvq::launch_kmeans(keys, batch, n, heads, head_dim, key_stride, head_stride,
+                                       batch_stride, centroids, n_centroids, iters, assign_out,
+                                       ws, (hipStream_t)stream));
+}
+
 size_t attn_int2_decode_workspace(const kvq_layout* L, int32_t q_heads, int32_t n_tokens) {
   if (check_layout(L) != KVQ_OK || q_heads < 1 || n_tokens < 1) return 0;
   return kvq::decode_workspace_bytes(L, q_heads, n_tokens);

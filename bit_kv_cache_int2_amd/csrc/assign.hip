@@ -5,6 +5,8 @@
 // weighted distances by the weighted error of its INT2 residual; the
 // residual is INT2-quantised per group of 32 and, with PSAC, its error is
 // projected on the query principal directions.
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -442,7 +444,7 @@ __global__ __launch_bounds__(256) void centroid_kernel(
     }
   }
   if (!TO_CACHE) {
-    idx_out[i] = bestj;
+    idx_out[bh * n + i] = bestj;
     return;
   }
   uint32_t codes[D / 16];
@@ -495,6 +497,195 @@ hipError_t launch_assign_t(const void* keys, int64_t n, int64_t stride, const fl
 }
 
 
+// Lloyd update.  The members of each centroid are first listed in key
+// order by a stable counting sort of the assignment (per chunk of 256 keys:
+// counts, a prefix over chunks and centroids, then a scatter ranked within
+// the chunk by ballots), then one block per centroid sums each channel of
+// its members in that order in fp64 and writes the f32 mean (no members:
+// the centroid is left as it is).
+constexpr int kSortChunk = 256;
+
+struct KmWs {          // workspace carve-up, per (sequence, head) blocks
+  int32_t* idx;        // [BH][n] assignment of the current round
+  int32_t* members;    // [BH][n] key indices grouped by centroid, key order
+  int32_t* cnt;        // [BH][nch][256] per-chunk counts, then offsets
+  int32_t* start;      // [BH][256] first slot of each centroid's members
+  int32_t* count;      // [BH][256] member counts
+};
+
+inline size_t km_align(size_t b) { return (b + 255) & ~(size_t)255; }
+
+inline int64_t km_chunks(int64_t n) { return (n + kSortChunk - 1) / kSortChunk; }
+
+// Bitmask of the lanes of this wave whose 8-bit value equals this lane's
+// (keys past the end hold 256 and match only each other).
+KVQ_DEV uint64_t match8(int32_t v) {
+  uint64_t m = __ballot(1);
+#pragma unroll
+  for (int bit = 0; bit < 9; ++bit) {          // bit 8: the "no key" mark
+    const bool set = (v >> bit) & 1;
+    const uint64_t b = __ballot(set);
+    m &= set ? b : ~b;
+  }
+  return m;
+}
+
+KVQ_DEV int rank_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+// counts of each centroid in chunk blockIdx.x of (sequence, head) bh
+__global__ __launch_bounds__(kSortChunk) void km_count_kernel(const int32_t* __restrict__ idx,
+                                                              int64_t n, int32_t* __restrict__ cnt) {
+  __shared__ int32_t h[256];
+  const int t = threadIdx.x;
+  const int64_t bh = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
+  const int64_t nch = gridDim.x;
+  h[t] = 0;
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * kSortChunk + t;
+  if (i < n) atomicAdd(&h[idx[bh * n + i]], 1);
+  __syncthreads();
+  cnt[(bh * nch + blockIdx.x) * 256 + t] = h[t];
+}
+
+// per (sequence, head): chunk counts -> global slots (centroid base + the
+// members of earlier chunks), centroid starts and counts
+__global__ __launch_bounds__(256) void km_offset_kernel(int64_t nch, int32_t* __restrict__ cnt,
+                                                        int32_t* __restrict__ start,
+                                                        int32_t* __restrict__ count) {
+  __shared__ int32_t sc[256];
+  const int j = threadIdx.x;
+  const int64_t bh = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  int32_t* c = cnt + bh * nch * 256 + j;
+  int32_t tot = 0;
+  for (int64_t ch = 0; ch < nch; ++ch) tot += c[ch * 256];
+  sc[j] = tot;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {     // inclusive scan over centroids
+    const int32_t v = j >= o ? sc[j - o] : 0;
+    __syncthreads();
+    sc[j] += v;
+    __syncthreads();
+  }
+  int32_t run = sc[j] - tot;
+  start[bh * 256 + j] = run;
+  count[bh * 256 + j] = tot;
+  for (int64_t ch = 0; ch < nch; ++ch) {
+    const int32_t v = c[ch * 256];
+    c[ch * 256] = run;
+    run += v;
+  }
+}
+
+// stable scatter of the key indices of chunk blockIdx.x to their slots
+__global__ __launch_bounds__(kSortChunk) void km_scatter_kernel(const int32_t* __restrict__ idx,
+                                                                int64_t n,
+                                                                const int32_t* __restrict__ cnt,
+                                                                int32_t* __restrict__ members) {
+  __shared__ int32_t wc[kSortChunk / 64][256];
+  const int t = threadIdx.x, w = t >> 6;
+  const int64_t bh = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
+  const int64_t nch = gridDim.x;
+  for (int e = t; e < (kSortChunk / 64) * 256; e += kSortChunk) (&wc[0][0])[e] = 0;
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * kSortChunk + t;
+  const int32_t j = i < n ? idx[bh * n + i] : 256;
+  const uint64_t m = match8(j);
+  const int r = rank_below(m);
+  if (j < 256 && r == 0) wc[w][j] = __builtin_popcountll(m);   // the group's first lane
+  __syncthreads();
+  if (j < 256) {
+    int32_t slot = cnt[(bh * nch + blockIdx.x) * 256 + j] + r;
+    for (int u = 0; u < w; ++u) slot += wc[u][j];
+    members[bh * n + slot] = (int32_t)i;
+  }
+}
+
+// One wave per centroid; lane l owns channels CPL*l .. CPL*l + CPL - 1.
+// Member rows are gathered kBatch at a time with no per-load branch (the
+// tail batch repeats the last member and drops it from the sum), and the
+// next batch's member indices are fetched while the rows are in flight.
+template <int D>
+__global__ __launch_bounds__(64) void km_mean_kernel(const uint16_t* __restrict__ keys_all,
+                                                     int64_t n, int64_t stride, int64_t head_stride,
+                                                     int64_t batch_stride,
+                                                     const int32_t* __restrict__ members,
+                                                     const int32_t* __restrict__ start,
+                                                     const int32_t* __restrict__ count,
+                                                     float* __restrict__ cent_all, int C) {
+  constexpr int CPL = D / 64;                  // 2 (head_dim 128) or 1 (64)
+  using W = typename std::conditional<CPL == 2, uint32_t, uint16_t>::type;
+  constexpr int kBatch = 32;
+  const int j = blockIdx.x, l = threadIdx.x;
+  const int64_t bh = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
+  const uint16_t* keys = keys_all + blockIdx.z * batch_stride + blockIdx.y * head_stride + CPL * l;
+  const int32_t m = count[bh * 256 + j];
+  if (m == 0) return;
+  const int32_t* mem = members + bh * n + start[bh * 256 + j];
+  double acc[CPL] = {};
+  int32_t r[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) r[u] = mem[u < m ? u : m - 1];
+  for (int e = 0; e < m; e += kBatch) {
+    W v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      v[u] = *reinterpret_cast<const W*>(keys + (int64_t)r[u] * stride);
+    const int e2 = e + kBatch;
+    if (e2 < m) {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) r[u] = mem[e2 + u < m ? e2 + u : m - 1];
+    }
+    // a dropped slot adds +0.0, which leaves the sum's bits unchanged: it
+    // starts at +0.0 and so is never -0.0
+    const int valid = m - e < kBatch ? m - e : kBatch;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const double x = (double)bf16_to_f32((uint16_t)((uint32_t)v[u] >> (16 * c)));
+        acc[c] += u < valid ? x : 0.0;
+      }
+    }
+  }
+  float* out = cent_all + (bh * C + j) * D + CPL * l;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) out[c] = (float)(acc[c] / (double)m);
+}
+
+template <int D>
+hipError_t launch_kmeans_d(const void* keys, int B, int64_t n, int H, int64_t stride,
+                           int64_t head_stride, int64_t batch_stride, float* cent, int C,
+                           int iters, int32_t* assign_out, const KmWs& ws, hipStream_t st) {
+  const dim3 agrid((unsigned)((n + 255) / 256), (unsigned)H, (unsigned)B);
+  const int64_t nch = km_chunks(n);
+  const dim3 sgrid((unsigned)nch, (unsigned)H, (unsigned)B);
+  auto assign = [&](int32_t* a) {
+    centroid_kernel<D, false, 0, false><<<agrid, 256, 0, st>>>(
+        (const uint16_t*)keys, stride, head_stride, batch_stride, n, cent, C, nullptr, 1,
+        nullptr, a, nullptr, nullptr, nullptr, nullptr, H, 0, 0);
+    return hipGetLastError();
+  };
+  for (int it = 0; it < iters; ++it) {
+    // the last round's assignment is the one reported
+    int32_t* a = (it == iters - 1 && assign_out) ? assign_out : ws.idx;
+    hipError_t e = assign(a);
+    if (e != hipSuccess) return e;
+    km_count_kernel<<<sgrid, kSortChunk, 0, st>>>(a, n, ws.cnt);
+    km_offset_kernel<<<dim3((unsigned)H, (unsigned)B), 256, 0, st>>>(nch, ws.cnt, ws.start,
+                                                                     ws.count);
+    km_scatter_kernel<<<sgrid, kSortChunk, 0, st>>>(a, n, ws.cnt, ws.members);
+    km_mean_kernel<D><<<dim3((unsigned)C, (unsigned)H, (unsigned)B), 64, 0, st>>>(
+        (const uint16_t*)keys, n, stride, head_stride, batch_stride, ws.members, ws.start,
+        ws.count, cent, C);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (iters == 0 && assign_out) return assign(assign_out);
+  return hipSuccess;
+}
+
 template <int D>
 hipError_t launch_centroid_append_d(const kvq_cache* c, const void* k, int cur_len, int n_new,
                                    hipStream_t st) {
@@ -526,6 +717,36 @@ hipError_t launch_cluster_assign(const void* keys, int64_t n, int head_dim,
                   : launch_assign_t<128, false>(keys, n, key_stride, centroids, n_centroids, nullptr, 1, idx_out, stream);
   return sens_w ? launch_assign_t<64, true>(keys, n, key_stride, centroids, n_centroids, sens_w, topk, idx_out, stream)
                 : launch_assign_t<64, false>(keys, n, key_stride, centroids, n_centroids, nullptr, 1, idx_out, stream);
+}
+
+size_t kmeans_workspace_bytes(int batch, int heads, int64_t n) {
+  const size_t bh = (size_t)batch * heads;
+  return km_align(bh * n * 4) * 2 + km_align(bh * km_chunks(n) * 256 * 4) +
+         km_align(bh * 256 * 4) * 2;
+}
+
+hipError_t launch_kmeans(const void* keys, int batch, int64_t n, int heads, int head_dim,
+                         int64_t key_stride, int64_t head_stride, int64_t batch_stride,
+                         float* centroids, int n_centroids, int iters, int32_t* assign_out,
+                         void* ws, hipStream_t stream) {
+  if (n == 0 || batch == 0 || heads == 0) return hipSuccess;
+  const size_t bh = (size_t)batch * heads;
+  char* p = (char*)ws;
+  KmWs w;
+  w.idx = (int32_t*)p;
+  p += km_align(bh * n * 4);
+  w.members = (int32_t*)p;
+  p += km_align(bh * n * 4);
+  w.cnt = (int32_t*)p;
+  p += km_align(bh * km_chunks(n) * 256 * 4);
+  w.start = (int32_t*)p;
+  p += km_align(bh * 256 * 4);
+  w.count = (int32_t*)p;
+  return head_dim == 128
+             ? launch_kmeans_d<128>(keys, batch, n, heads, key_stride, head_stride, batch_stride,
+                                    centroids, n_centroids, iters, assign_out, w, stream)
+             : launch_kmeans_d<64>(keys, batch, n, heads, key_stride, head_stride, batch_stride,
+                                   centroids, n_centroids, iters, assign_out, w, stream);
 }
 
 }  // namespace kvq

@@ -22,6 +22,14 @@ hipError_t launch_cluster_assign(const void* keys, int64_t n, int head_dim,
                                  int n_centroids, const float* sens_w, int topk,
                                  int32_t* idx_out, hipStream_t stream);
 
+// Lloyd k-means of every (sequence, head) key set (assignment + fp64 mean
+// update per round) in a workspace of kmeans_workspace_bytes() bytes.
+size_t kmeans_workspace_bytes(int batch, int heads, int64_t n);
+hipError_t launch_kmeans(const void* keys, int batch, int64_t n, int heads, int head_dim,
+                         int64_t key_stride, int64_t head_stride, int64_t batch_stride,
+                         float* centroids, int n_centroids, int iters, int32_t* assign_out,
+                         void* ws, hipStream_t stream);
+
 // Number of token splits the decode uses, and the workspace they need.
 int decode_splits(const kvq_layout* L, int q_heads, int n_tokens);
 size_t decode_workspace_bytes(const kvq_layout* L, int q_heads, int n_tokens);

@@ -195,6 +195,33 @@ int kv_cluster_assign(const void* keys_bf16_dev, int64_t n, int32_t head_dim,
                       int32_t n_centroids, const float* sens_w_dev,
                       int32_t topk, int32_t* idx_out_dev, void* stream);
 
+/* ------------------------------------------------------------ k-means */
+/* Lloyd k-means of the keys of each (sequence, head) ([QWM] 1: the cluster
+ * centres come from clustering keys; a calibration step before the hot
+ * path), giving the per-(sequence, kv head) centroid tables of a
+ * centroid-key cache.  Each of `iters` rounds assigns every key with the
+ * KVQ_KEY_CENTROID rule of kv_cluster_assign and then sets each centroid to
+ * the f32 value of the fp64 mean of its members, summed in key order; a
+ * centroid without members keeps its value.  Key i of head h of sequence b
+ * is the bf16 vector (head_dim contiguous elements) at keys_bf16_dev +
+ * b * batch_stride + i * key_stride + h * head_stride elements (the
+ * append input [B][n][H][D] has key_stride H*D, head_stride D, batch_stride
+ * n*H*D).  centroids_dev f32 [batch][heads][n_centroids][head_dim]: read as
+ * the starting tables, overwritten with the result.  assign_out_dev i32
+ * [batch][heads][n] (nullable): the last round's assignment (with iters ==
+ * 0, the assignment to the starting tables).  ws_dev: at least
+ * kv_kmeans_workspace(batch, heads, n) bytes of device memory, 256-byte
+ * aligned, in use until the stream passes the call (it holds the
+ * assignment and the member lists of the rounds).  All work is enqueued on `stream`.  Errors:
+ * KVQ_EINVAL (negative sizes or strides, iters < 0, nulls, misaligned
+ * pointers, key_stride < head_dim), KVQ_EUNSUPPORTED (head_dim not 64/128,
+ * n_centroids outside 1..256), KVQ_EWORKSPACE (missing or short ws). */
+size_t kv_kmeans_workspace(int32_t batch, int32_t heads, int64_t n);
+int kv_kmeans(const void* keys_bf16_dev, int32_t batch, int64_t n, int32_t heads,
+              int32_t head_dim, int64_t key_stride, int64_t head_stride, int64_t batch_stride,
+              float* centroids_dev, int32_t n_centroids, int32_t iters,
+              int32_t* assign_out_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------ decode */
 /* Workspace bytes attn_int2_decode needs for these sizes. */
 size_t attn_int2_decode_workspace(const kvq_layout* L, int32_t q_heads,

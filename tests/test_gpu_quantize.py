@@ -163,6 +163,51 @@ def test_cluster_assign_exact_scan_paths():
     _assign_check(keys, cent, wn, 4, tag="negative weight")
 
 
+@pytest.mark.parametrize("D,C,n,iters", [(128, 64, 3000, 3), (64, 16, 512, 4), (128, 256, 4100, 2),
+                                         (128, 32, 700, 0)])
+def test_kmeans_matches_oracle(D, C, n, iters):
+    """GPU Lloyd rounds give the oracle's centroids and last assignment bit
+    for bit; duplicated starting picks leave a centroid without members."""
+    rng = np.random.default_rng(21 + C)
+    base = rng.standard_normal((C, D)).astype(np.float32)
+    keys = synth.to_bf16_bits((base[rng.integers(0, C, n)] + 0.7 * rng.standard_normal((n, D))).astype(np.float32))
+    kf = synth.bf16_bits_to_f32(keys)
+    init = rng.choice(n, C, replace=False).astype(np.int64)
+    init[C - 1] = init[0]                       # a duplicate pick: its cluster stays empty
+    want_c, want_a = oracle.kmeans(kf, C, init, iters)
+    cent = torch.from_numpy(np.ascontiguousarray(kf[init])).cuda()
+    # rows strided inside a wider matrix
+    wide = np.zeros((n, 2 * D), np.uint16)
+    wide[:, :D] = keys
+    kt = dev_bf16(wide)[:, :D]
+    got_c, got_a = kv.kv_kmeans(kt, cent, iters)
+    got_c, got_a = got_c.cpu().numpy(), got_a.cpu().numpy()
+    assert np.array_equal(got_a, want_a), f"assignment: {np.sum(got_a != want_a)} keys differ"
+    assert np.array_equal(got_c.view(np.uint32), want_c.view(np.uint32)), \
+        f"centroids: {np.sum(got_c != want_c)} values differ"
+
+
+def test_kmeans_batched_heads_match_oracle():
+    """One call over [B, n, H, D] keys runs every (sequence, head) table's
+    rounds; each equals the oracle's k-means of that key set."""
+    B, n, H, D, C, iters = 2, 1500, 3, 128, 48, 2
+    rng = np.random.default_rng(77)
+    keys = synth.to_bf16_bits(rng.standard_normal((B, n, H, D)).astype(np.float32) *
+                              rng.uniform(0.5, 2.0, (1, 1, H, 1)).astype(np.float32))
+    kf = synth.bf16_bits_to_f32(keys)
+    init = np.stack([np.stack([rng.choice(n, C, replace=False) for _ in range(H)]) for _ in range(B)])
+    start = np.stack([np.stack([kf[b, init[b, h], h] for h in range(H)]) for b in range(B)])
+    cent = torch.from_numpy(np.ascontiguousarray(start)).cuda()
+    got_c, got_a = kv.kv_kmeans(dev_bf16(keys), cent, iters)
+    got_c, got_a = got_c.cpu().numpy(), got_a.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            want_c, want_a = oracle.kmeans(np.ascontiguousarray(kf[b, :, h]), C, init[b, h], iters)
+            assert np.array_equal(got_a[b, h], want_a), f"(b={b}, h={h}) assignment"
+            assert np.array_equal(got_c[b, h].view(np.uint32), want_c.view(np.uint32)), \
+                f"(b={b}, h={h}) centroids"
+
+
 @pytest.mark.slow
 def test_llm_decode_build_full_size_sampled():
     """Full 16 x 32768 x 8-head window-key build (the benchmark's launch
