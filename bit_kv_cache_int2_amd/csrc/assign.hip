@@ -70,22 +70,52 @@ KVQ_DEV float residual_q2(const float (&k)[D], const float* __restrict__ c,
 // Exact squared distance of key row kr (bf16) to centroid row cr (fp32): the
 // fp32 sum in channel order with fma, t = k - c; QSAC weighs each term as
 // fma(w t, t) with w t rounded first.
-template <int D, bool QSAC>
+// All rows' loads are issued before the sum when ALL (one memory round
+// trip; the queue drain, where nothing else is live), else 32 channels at a
+// time.
+template <int D, bool QSAC, bool ALL = false>
 KVQ_DEV float exact_dist(const uint16_t* __restrict__ kr, const float* __restrict__ cr, const float* w) {
+  constexpr int kStep = ALL ? D : 32;
   float acc = 0.0f;
-#pragma unroll 4
-  for (int d = 0; d < D; d += 8) {
-    float x[8];
-    bf16x8_to_f32(*reinterpret_cast<const uint4*>(kr + d), x);
-    const float4 c0 = *reinterpret_cast<const float4*>(cr + d), c1 = *reinterpret_cast<const float4*>(cr + d + 4);
-    const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll 1
+  for (int d0 = 0; d0 < D; d0 += kStep) {
+    uint4 kv[kStep / 8];
+    float4 cv[kStep / 4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float t = x[u] - cc[u];
-      acc = QSAC ? __builtin_fmaf(w[d + u] * t, t, acc) : __builtin_fmaf(t, t, acc);
+    for (int u = 0; u < kStep / 8; ++u) kv[u] = *reinterpret_cast<const uint4*>(kr + d0 + 8 * u);
+#pragma unroll
+    for (int u = 0; u < kStep / 4; ++u) cv[u] = *reinterpret_cast<const float4*>(cr + d0 + 4 * u);
+#pragma unroll
+    for (int u = 0; u < kStep / 8; ++u) {
+      float x[8];
+      bf16x8_to_f32(kv[u], x);
+      const float cc[8] = {cv[2 * u].x, cv[2 * u].y, cv[2 * u].z, cv[2 * u].w,
+                           cv[2 * u + 1].x, cv[2 * u + 1].y, cv[2 * u + 1].z, cv[2 * u + 1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = x[e] - cc[e];
+        const int d = d0 + 8 * u + e;
+        acc = QSAC ? __builtin_fmaf(w[d] * t, t, acc) : __builtin_fmaf(t, t, acc);
+      }
     }
   }
   return acc;
+}
+
+// Two floats to bf16 (round to nearest even), packed low = a, high = b.
+KVQ_DEV uint32_t bf16_pack2(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, b2));
+}
+
+// Rescoring queue entry: the top 18 bits of a float at most the pair's
+// lower end (a NaN end counts as -inf, so the pair is kept), the key's slot
+// in the wave (6 bits) and the centroid index (8 bits).
+KVQ_DEV uint32_t queue_entry(float lower, int kl, int j) {
+  uint32_t b = __float_as_uint(lower != lower ? -__builtin_inff() : lower);
+  if ((b >> 31) && (b & 0x3FFFu)) b += 0x4000u;   // negative: round the magnitude up
+  return (b & 0xFFFFC000u) | ((uint32_t)kl << 8) | (uint32_t)j;
 }
 
 // Distance (bits, non-negative) and index packed so that the u64 order is
@@ -130,7 +160,7 @@ constexpr float kMarginRel = 1.0f / 4096.0f;
 constexpr float kMarginAbs = 1e-30f;
 
 template <int D, bool QSAC, int R, bool TO_CACHE>
-__global__ __launch_bounds__(256) void centroid_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void centroid_kernel(
     const uint16_t* __restrict__ kin, int64_t key_stride, int64_t head_stride,
     int64_t batch_stride, int64_t n, const float* __restrict__ cent, int C,
     const float* __restrict__ sens_w, int topk, const float* __restrict__ basis,
@@ -149,6 +179,9 @@ __global__ __launch_bounds__(256) void centroid_kernel(
   __shared__ unsigned long long best[QSAC ? 1 : 256];
   __shared__ unsigned long long clist[QSAC ? 256 * kList : 1];
   __shared__ int ccount[QSAC ? 256 : 1];
+  __shared__ float thrf[256];     // final threshold U + 2 Mk per key
+  __shared__ int nsurv[256];      // queue entries per key that pass it
+  __shared__ uint32_t sj[QSAC ? 1 : 256];   // their lowest centroid index
   __shared__ int bad_w;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -165,7 +198,11 @@ __global__ __launch_bounds__(256) void centroid_kernel(
     for (int d = tid; d < D * R; d += 256) ul[d] = basis[bh * D * R + d];
   if (tid == 0) bad_w = 0;
   if (QSAC) ccount[tid] = 0;
-  else best[tid] = ~0ull;
+  else {
+    best[tid] = ~0ull;
+    sj[tid] = ~0u;
+  }
+  nsurv[tid] = 0;
   if (lane == 0) qcount[wave] = 0;
   __syncthreads();
   if (QSAC && tid < D && !(wl[tid] >= 0.0f && wl[tid] < __builtin_inff())) bad_w = 1;
@@ -181,11 +218,12 @@ __global__ __launch_bounds__(256) void centroid_kernel(
   for (int nt = 0; nt < 4; ++nt) {
     const int64_t i = kbase + nt * 16 + c16;
     kok[nt] = i < n;
+    // slots past the end read the last key; they never push a candidate
+    const uint16_t* krow = kb + (kok[nt] ? i : n - 1) * key_stride;
     float s2 = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const uint4 u = kok[nt] ? *reinterpret_cast<const uint4*>(kb + i * key_stride + ks * 32 + 8 * g)
-                              : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 u = *reinterpret_cast<const uint4*>(krow + ks * 32 + 8 * g);
       kop[nt][ks] = __builtin_bit_cast(bf8, u);
       float x[8];
       bf16x8_to_f32(u, x);
@@ -210,23 +248,26 @@ __global__ __launch_bounds__(256) void centroid_kernel(
     {
       // thread -> row tid / 4, a quarter of its channels
       const int r = tid >> 2, q = tid & 3, j = c0 + r;
+      // rows past the table repeat the last row; their bounds are +inf
+      const float* crow = cb + (int64_t)(j < C ? j : C - 1) * D;
       float s2 = 0.0f;
 #pragma unroll
       for (int d = q * (D / 4); d < (q + 1) * (D / 4); d += 4) {
-        const float4 v = (j < C) ? *reinterpret_cast<const float4*>(cb + (int64_t)j * D + d)
-                                 : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        const float4 v = *reinterpret_cast<const float4*>(crow + d);
         const float x[4] = {v.x, v.y, v.z, v.w};
-        __bf16 hv[4], lv[4];
+        float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float y = QSAC ? wl[d + e] * x[e] : x[e];
-          s2 = __builtin_fmaf(y, x[e], s2);
-          hv[e] = (__bf16)y;
-          lv[e] = (__bf16)(y - (float)hv[e]);
+          y[e] = QSAC ? wl[d + e] * x[e] : x[e];
+          s2 = __builtin_fmaf(y[e], x[e], s2);
         }
-        typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
-        *reinterpret_cast<bf4*>(&chi[r * CP + d]) = bf4{hv[0], hv[1], hv[2], hv[3]};
-        *reinterpret_cast<bf4*>(&clo[r * CP + d]) = bf4{lv[0], lv[1], lv[2], lv[3]};
+        // hi = bf16(y) (round to nearest even), lo = bf16(y - hi)
+        const uint2 hb = make_uint2(bf16_pack2(y[0], y[1]), bf16_pack2(y[2], y[3]));
+        const float h[4] = {__uint_as_float(hb.x << 16), __uint_as_float(hb.x & 0xFFFF0000u),
+                            __uint_as_float(hb.y << 16), __uint_as_float(hb.y & 0xFFFF0000u)};
+        const uint2 lb = make_uint2(bf16_pack2(y[0] - h[0], y[1] - h[1]), bf16_pack2(y[2] - h[2], y[3] - h[3]));
+        *reinterpret_cast<uint2*>(&chi[r * CP + d]) = hb;
+        *reinterpret_cast<uint2*>(&clo[r * CP + d]) = lb;
       }
       s2 += __shfl_xor(s2, 1, 64);
       s2 += __shfl_xor(s2, 2, 64);
@@ -315,37 +356,70 @@ __global__ __launch_bounds__(256) void centroid_kernel(
       }
       U[nt] = fminf(U[nt], uu);
       const float thr = U[nt] + 2.0f * mk[nt];
+      // candidate mask, bit 4 mt + i (a NaN bound counts as a candidate;
+      // rows past the table are +inf)
+      uint32_t cm = 0;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // a NaN bound counts as a candidate; rows past the table are +inf
-          if (kok[nt] && !(vl[mt][i] > thr)) {
-            const int j = c0 + mt * 16 + 4 * g + i;
-            const int pos = atomicAdd(&qcount[wave], 1);
-            if (pos < kQueue) queue[wave][pos] = ((uint32_t)(nt * 16 + c16) << 16) | (uint32_t)j;
-          }
+        for (int i = 0; i < 4; ++i) cm |= (uint32_t)!(vl[mt][i] > thr) << (4 * mt + i);
+      if (!kok[nt]) cm = 0;
+      if (__ballot(cm != 0)) {
+        while (cm) {
+          const int b = __builtin_ctz(cm);
+          cm &= cm - 1;
+          const int j = c0 + (b >> 2) * 16 + 4 * g + (b & 3);
+          float vb = vl[0][0];   // vl[b / 4][b % 4], selected without a register index
+#pragma unroll
+          for (int q = 1; q < 16; ++q) vb = b == q ? vl[q >> 2][q & 3] : vb;
+          const int pos = atomicAdd(&qcount[wave], 1);
+          if (pos < kQueue) queue[wave][pos] = queue_entry(vb, nt * 16 + c16, j);
         }
+      }
     }
   }
 
-  // ---- drain the queue once: exact distances, lanes in parallel
+  // ---- drain the queue once.  Entries whose lower end exceeds the key's
+  // final threshold cannot win (plain) or be in the top 4 (QSAC) and are
+  // dropped.  Plain: a key with a single entry left has its winner without
+  // rescoring (the winner's lower end never exceeds the final threshold);
+  // the others are rescored exactly, lanes in parallel.
+  if (g == 0) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) thrf[wave * 64 + nt * 16 + c16] = U[nt] + 2.0f * mk[nt];
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
   const int cnt = __builtin_amdgcn_readfirstlane(qcount[wave]);
   const bool overflow = cnt > kQueue;   // wave-uniform
+  auto live = [&](uint32_t ent) {       // j past the table: only when every bound was infinite
+    const int kl = (int)((ent >> 8) & 63u), j = (int)(ent & 255u);
+    return j < C && !(__uint_as_float(ent & 0xFFFFC000u) > thrf[wave * 64 + kl]);
+  };
   if (!overflow && !exact_scan) {
     for (int e = lane; e < cnt; e += 64) {
       const uint32_t ent = queue[wave][e];
-      const int kl = (int)(ent >> 16), j = (int)(ent & 0xFFFFu);
-      if (j >= C) continue;   // only when every bound was infinite
-      const float dist = exact_dist<D, QSAC>(kb + (kbase + kl) * key_stride, cb + (int64_t)j * D, wl);
-      if (QSAC) {
-        const int pos = atomicAdd(&ccount[wave * 64 + kl], 1);
-        if (pos < kList) clist[(wave * 64 + kl) * kList + pos] = dist_key(dist, j);
-      } else {
-        atomicMin(&best[wave * 64 + kl], dist_key(dist, j));
+      if (live(ent)) {
+        const int kl = (int)((ent >> 8) & 63u);
+        atomicAdd(&nsurv[wave * 64 + kl], 1);
+        if (!QSAC) atomicMin(&sj[wave * 64 + kl], ent & 255u);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    for (int e = lane; e < cnt; e += 64) {
+      const uint32_t ent = queue[wave][e];
+      const int kl = (int)((ent >> 8) & 63u), j = (int)(ent & 255u);
+      if (live(ent) && (QSAC || nsurv[wave * 64 + kl] > 1)) {
+        const float dist = exact_dist<D, QSAC, true>(kb + (kbase + kl) * key_stride, cb + (int64_t)j * D, wl);
+        if (QSAC) {
+          const int pos = atomicAdd(&ccount[wave * 64 + kl], 1);
+          if (pos < kList) clist[(wave * 64 + kl) * kList + pos] = dist_key(dist, j);
+        } else {
+          atomicMin(&best[wave * 64 + kl], dist_key(dist, j));
+        }
       }
     }
   }
@@ -394,7 +468,8 @@ __global__ __launch_bounds__(256) void centroid_kernel(
       }
     }
   } else if (!QSAC && !scan) {
-    bestj = (int)(best[wave * 64 + lane] & 0xFFFFFFFFull);
+    bestj = nsurv[wave * 64 + lane] == 1 ? (int)sj[wave * 64 + lane]
+                                         : (int)(best[wave * 64 + lane] & 0xFFFFFFFFull);
   }
   if (scan) {
     // every centroid, in index order, with the rule's arithmetic
