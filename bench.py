@@ -238,10 +238,15 @@ def chunk_workload(name: str, steps: int, warmup: int) -> dict:
     return rec
 
 
-def kmeans_workload(steps: int, warmup: int) -> dict:
+KMEANS_SAMPLE_HEADS = 16   # oracle leg: this many heads, one round each
+
+
+def kmeans_workload(steps: int, warmup: int, with_cpu: bool = True) -> dict:
     """Calibration: Lloyd rounds of kv_kmeans over the video workload's
     cached keys (40 heads x 31200 keys, 256 centroids, head_dim 128); one
-    step = one round for every head, each head starting from its picks."""
+    step = one round for every head (one call), each head starting from its
+    picks.  The roofline is the assignment kernel's, timed on its own (a call
+    with zero rounds is exactly one assignment launch)."""
     import numpy as np
     import torch
 
@@ -253,7 +258,7 @@ def kmeans_workload(steps: int, warmup: int) -> dict:
     C = 256
     kd = torch.from_numpy(np.ascontiguousarray(d["K"]).view(np.int16)).view(torch.bfloat16).cuda()
     K = synth.bf16_bits_to_f32(d["K"])[0]
-    D = K.shape[-1]
+    Dh = K.shape[-1]
     init = torch.from_numpy(np.ascontiguousarray(
         np.stack([K[d["kmeans_init"][0, h], h] for h in range(H)]))).cuda()[None]   # [1][H][C][D]
     cent = init.clone()
@@ -261,30 +266,56 @@ def kmeans_workload(steps: int, warmup: int) -> dict:
     ws = torch.empty(kv.lib().kv_kmeans_workspace(1, H, T), dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
 
+    def timed(fn, n):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record()
+        for _ in range(n):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e-3 / n, time.perf_counter() - t0
+
     def step():    # one call: every head's round
         cent.copy_(init)
         kv.kv_kmeans(kd, cent, 1, assign_out=asg, workspace=ws)
 
+    def assign_only():
+        kv.kv_kmeans(kd, init, 0, assign_out=asg, workspace=ws)
+
     for _ in range(warmup):
         step()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    t = ev0.elapsed_time(ev1) * 1e-3 / steps
-    return {"metric": "k-means round time (all heads)", "value": round(t * 1e6, 1), "unit": "us",
-            "n_gpus": 1, "steps": steps, "warmup": warmup,
-            "ms_per_step": round(wall / steps * 1e3, 4), "higher_is_better": False,
-            "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
-            "config": {"workload": "kmeans", "heads": H, "keys_per_head": T, "centroids": C,
-                       "head_dim": D, "rule": "exact fp32 assignment, fp64 key-order means"},
-            "kmeans": {"us_per_round": round(t * 1e6, 1),
-                       "g_key_assignments_s": round(H * T / t / 1e9, 3)}}
+        assign_only()
+    t, wall = timed(step, steps)
+    t_as, _ = timed(assign_only, steps)
+    # the products k.c of every (key, centroid) pair, 2 flops each
+    flops = 2.0 * H * T * C * Dh
+    tfs = flops / t_as / 1e12
+    rec = {"metric": "k-means round time (all heads)", "value": round(t * 1e6, 1), "unit": "us",
+           "n_gpus": 1, "steps": steps, "warmup": warmup,
+           "ms_per_step": round(wall / steps * 1e3, 4), "higher_is_better": False,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16+fp32", "data": "synthetic",
+           "config": {"workload": "kmeans", "heads": H, "keys_per_head": T, "centroids": C,
+                      "head_dim": Dh, "rule": "exact fp32 assignment, fp64 key-order means"},
+           "kmeans": {"us_per_round": round(t * 1e6, 1), "assign_us": round(t_as * 1e6, 1),
+                      "update_us": round((t - t_as) * 1e6, 1),
+                      "g_key_assignments_s": round(H * T / t_as / 1e9, 3)},
+           "roofline": {"kernel": "centroid_kernel", "bound": "mfma", "achieved": round(tfs, 2),
+                        "peak": MFMA_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / MFMA_PEAK_TFS, 4),
+                        "traffic": None}}
+    if with_cpu:
+        import oracle
+        S = KMEANS_SAMPLE_HEADS
+        t0 = time.perf_counter()
+        for h in range(S):
+            oracle.kmeans(np.ascontiguousarray(K[:, h]), C, d["kmeans_init"][0, h], 1)
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(dt * H / S * 1e6, 1), "unit": "us",
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "sample": f"{S} of {H} heads, one round each ({T} keys, {C} centroids): "
+                                         f"{dt:.2f} s, scaled to {H} heads"}
+    return rec
 
 
 def main() -> int:
@@ -305,8 +336,8 @@ def main() -> int:
     if args.workload != "llm_decode":
         import torch
         torch.cuda.set_device(0)
-        run = kmeans_workload if args.workload == "kmeans" else (
-            lambda s, w: chunk_workload(args.workload, s, w))
+        run = (lambda s, w: kmeans_workload(s, w, not args.no_cpu_baseline)) if args.workload == "kmeans" \
+            else (lambda s, w: chunk_workload(args.workload, s, w))
         print(json.dumps(run(args.steps, args.warmup)), flush=True)
         return 0
 

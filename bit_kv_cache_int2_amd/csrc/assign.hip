@@ -625,28 +625,39 @@ __global__ __launch_bounds__(kSortChunk) void km_count_kernel(const int32_t* __r
 }
 
 // per (sequence, head): chunk counts -> global slots (centroid base + the
-// members of earlier chunks), centroid starts and counts
-__global__ __launch_bounds__(256) void km_offset_kernel(int64_t nch, int32_t* __restrict__ cnt,
-                                                        int32_t* __restrict__ start,
-                                                        int32_t* __restrict__ count) {
+// members of earlier chunks), centroid starts and counts.  Thread (q, j)
+// covers centroid j over quarter q of the chunks.
+__global__ __launch_bounds__(1024) void km_offset_kernel(int64_t nch, int32_t* __restrict__ cnt,
+                                                         int32_t* __restrict__ start,
+                                                         int32_t* __restrict__ count) {
+  __shared__ int32_t part[4][256];
   __shared__ int32_t sc[256];
-  const int j = threadIdx.x;
+  const int j = threadIdx.x & 255, q = threadIdx.x >> 8;
   const int64_t bh = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const int64_t per = (nch + 3) / 4, c0 = q * per, c1 = min(nch, c0 + per);
   int32_t* c = cnt + bh * nch * 256 + j;
   int32_t tot = 0;
-  for (int64_t ch = 0; ch < nch; ++ch) tot += c[ch * 256];
-  sc[j] = tot;
+#pragma unroll 8
+  for (int64_t ch = c0; ch < c1; ++ch) tot += c[ch * 256];
+  part[q][j] = tot;
+  __syncthreads();
+  if (q == 0) {
+    const int32_t t = part[0][j] + part[1][j] + part[2][j] + part[3][j];
+    sc[j] = t;
+    count[bh * 256 + j] = t;
+  }
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {     // inclusive scan over centroids
-    const int32_t v = j >= o ? sc[j - o] : 0;
+    const int32_t v = (q == 0 && j >= o) ? sc[j - o] : 0;
     __syncthreads();
-    sc[j] += v;
+    if (q == 0) sc[j] += v;
     __syncthreads();
   }
-  int32_t run = sc[j] - tot;
-  start[bh * 256 + j] = run;
-  count[bh * 256 + j] = tot;
-  for (int64_t ch = 0; ch < nch; ++ch) {
+  int32_t run = sc[j] - (part[0][j] + part[1][j] + part[2][j] + part[3][j]);
+  if (q == 0) start[bh * 256 + j] = run;
+  for (int u = 0; u < q; ++u) run += part[u][j];
+#pragma unroll 8
+  for (int64_t ch = c0; ch < c1; ++ch) {
     const int32_t v = c[ch * 256];
     c[ch * 256] = run;
     run += v;
@@ -748,7 +759,7 @@ hipError_t launch_kmeans_d(const void* keys, int B, int64_t n, int H, int64_t st
     hipError_t e = assign(a);
     if (e != hipSuccess) return e;
     km_count_kernel<<<sgrid, kSortChunk, 0, st>>>(a, n, ws.cnt);
-    km_offset_kernel<<<dim3((unsigned)H, (unsigned)B), 256, 0, st>>>(nch, ws.cnt, ws.start,
+    km_offset_kernel<<<dim3((unsigned)H, (unsigned)B), 1024, 0, st>>>(nch, ws.cnt, ws.start,
                                                                      ws.count);
     km_scatter_kernel<<<sgrid, kSortChunk, 0, st>>>(a, n, ws.cnt, ws.members);
     km_mean_kernel<D><<<dim3((unsigned)C, (unsigned)H, (unsigned)B), 64, 0, st>>>(
