@@ -56,15 +56,15 @@ def lib():
     L.orc_wht_f64.restype = None
     L.orc_assign_plain.argtypes = [vp, vp, i32, i32]
     L.orc_assign_plain.restype = i32
-    L.orc_assign_qsac.argtypes = [vp, vp, i32, i32, vp, i32]
+    L.orc_assign_qsac.argtypes = [vp, vp, i32, i32, vp, i32, i32]
     L.orc_assign_qsac.restype = i32
-    L.orc_quantize_append.argtypes = [i32] * 9 + [vp] * 10 + [vp, vp, i32, i32]
+    L.orc_quantize_append.argtypes = [i32] * 11 + [vp] * 12 + [vp, vp, i32, i32]
     L.orc_quantize_append.restype = i32
     L.orc_dequant_keys.argtypes = [i32] * 6 + [vp] * 5 + [i32, i32, i32, vp]
     L.orc_dequant_keys.restype = None
     L.orc_dequant_values.argtypes = [i32, i32, i32, vp, vp, i32, i32, i32, vp]
     L.orc_dequant_values.restype = None
-    L.orc_attention.argtypes = ([i32] * 8 + [vp] * 9 + [i32, vp, i32, i32, dbl, vp, vp])
+    L.orc_attention.argtypes = ([i32] * 9 + [vp] * 11 + [i32, vp, i32, i32, dbl, vp, vp])
     L.orc_attention.restype = i32
     L.orc_merge.argtypes = [i32, i32, vp, vp, vp, vp, vp]
     L.orc_merge.restype = None
@@ -145,11 +145,17 @@ def assign_plain(k: np.ndarray, cent: np.ndarray) -> int:
     return int(lib().orc_assign_plain(_p(k), _p(cent), cent.shape[0], k.size))
 
 
-def assign_qsac(k: np.ndarray, cent: np.ndarray, w: np.ndarray, topk: int) -> int:
+QSAC_EXACT, QSAC_RANGE = 0, 1     # QSAC perturbation estimate
+PSAC_F16, PSAC_INT8 = 0, 1        # PSAC coefficient format
+
+
+def assign_qsac(k: np.ndarray, cent: np.ndarray, w: np.ndarray, topk: int,
+                score: int = QSAC_EXACT) -> int:
     k = np.ascontiguousarray(k, np.float32)
     cent = np.ascontiguousarray(cent, np.float32)
     w = np.ascontiguousarray(w, np.float32)
-    return int(lib().orc_assign_qsac(_p(k), _p(cent), cent.shape[0], k.size, _p(w), int(topk)))
+    return int(lib().orc_assign_qsac(_p(k), _p(cent), cent.shape[0], k.size, _p(w), int(topk),
+                                     int(score)))
 
 
 def merge(m: np.ndarray, l: np.ndarray, o: np.ndarray):
@@ -205,6 +211,8 @@ class Cache:
     C: int = 0
     topk: int = 1
     R: int = 0
+    qsac_score: int = 0        # QSAC_EXACT / QSAC_RANGE
+    psac_fmt: int = 0          # PSAC_F16 / PSAC_INT8
     k_codes: np.ndarray = field(default=None, repr=False)
     k_params: np.ndarray = field(default=None, repr=False)
     k_tail: np.ndarray = field(default=None, repr=False)
@@ -213,6 +221,8 @@ class Cache:
     sens_w: np.ndarray = field(default=None, repr=False)
     psac_basis: np.ndarray = field(default=None, repr=False)
     k_psac: np.ndarray = field(default=None, repr=False)
+    k_psac8: np.ndarray = field(default=None, repr=False)
+    k_psac_sc: np.ndarray = field(default=None, repr=False)
     v_codes: np.ndarray = field(default=None, repr=False)
     v_params: np.ndarray = field(default=None, repr=False)
 
@@ -241,10 +251,15 @@ class Cache:
             self.psac_basis = z((B, H, D, max(self.R, 1)), np.float32)
         if self.k_psac is None:
             self.k_psac = z((B, H, T, max(self.R, 1)), np.uint16)
+        if self.k_psac8 is None:
+            self.k_psac8 = z((B, H, T, max(self.R, 1)), np.int8)
+        if self.k_psac_sc is None:
+            self.k_psac_sc = z((B, H, T), np.uint16)
 
     def bufs(self):
         return [self.k_codes, self.k_params, self.k_tail, self.k_idx, self.centroids,
-                self.sens_w, self.psac_basis, self.k_psac, self.v_codes, self.v_params]
+                self.sens_w, self.psac_basis, self.k_psac, self.k_psac8, self.k_psac_sc,
+                self.v_codes, self.v_params]
 
     def append(self, k_bf16: np.ndarray, v_bf16: np.ndarray, cur_len: int) -> None:
         """Quantise tokens [cur_len, cur_len + n_new) of every sequence; inputs
@@ -255,7 +270,8 @@ class Cache:
         assert (B, H, D) == (self.B, self.H, self.D) and v.shape == k.shape
         rc = lib().orc_quantize_append(
             self.B, self.H, self.D, self.Tcap, self.key_mode, self.value_mode,
-            self.C, self.topk, self.R, *[_p(b) for b in self.bufs()],
+            self.C, self.topk, self.R, self.qsac_score, self.psac_fmt,
+            *[_p(b) for b in self.bufs()],
             _p(k), _p(v), int(cur_len), int(n_new))
         if rc != 0:
             raise ValueError(f"orc_quantize_append failed: {rc}")
@@ -281,10 +297,10 @@ class Cache:
         lse = np.empty((B, Hq, Lq), np.float64)
         rc = lib().orc_attention(
             self.B, self.H, self.D, self.Tcap, self.key_mode, self.value_mode,
-            max(self.C, 1), self.R, _p(self.k_codes), _p(self.k_params), _p(self.k_tail),
-            _p(self.k_idx), _p(self.centroids), _p(self.psac_basis), _p(self.k_psac),
-            _p(self.v_codes), _p(self.v_params), int(n), _p(q), Lq, Hq, float(scale),
-            _p(out), _p(lse))
+            max(self.C, 1), self.R, self.psac_fmt, _p(self.k_codes), _p(self.k_params),
+            _p(self.k_tail), _p(self.k_idx), _p(self.centroids), _p(self.psac_basis),
+            _p(self.k_psac), _p(self.k_psac8), _p(self.k_psac_sc), _p(self.v_codes),
+            _p(self.v_params), int(n), _p(q), Lq, Hq, float(scale), _p(out), _p(lse))
         if rc != 0:
             raise ValueError(f"orc_attention failed: {rc}")
         return out, lse
@@ -293,4 +309,5 @@ class Cache:
         """A one-sequence, one-head copy (for sampled checks at full size)."""
         sl = lambda a: np.ascontiguousarray(a[b:b + 1, h:h + 1])
         return Cache(1, 1, self.D, self.Tcap, self.key_mode, self.value_mode, self.C,
-                     self.topk, self.R, *[sl(a) for a in self.bufs()])
+                     self.topk, self.R, self.qsac_score, self.psac_fmt,
+                     *[sl(a) for a in self.bufs()])

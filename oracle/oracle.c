@@ -232,14 +232,40 @@ static void residual_q2(const float* k, const float* c, int D, uint8_t* codes,
   }
 }
 
+/* Range-based perturbation estimate of one candidate ([QWM] 1: from the
+ * residual groups' dynamic range and the query sensitivity): INT2 rounding
+ * noise has variance s^2/12 per element of a group with step s, weighted by
+ * the group's summed sensitivity W_g.  The common factor 1/12 is left out
+ * (it does not change which candidate is smallest):
+ *   W_g = fold acc = acc + w_d over the group's channels in order (fp32),
+ *   s_g = f32(f16((max r - min r) / 3)), the step the quantizer stores,
+ *   E = fold over groups in order of acc = fma(s_g * s_g, W_g, acc). */
+static float range_estimate(const float* k, const float* c, const float* w, int D) {
+  float E = 0.0f;
+  for (int g = 0; g < D / GROUP; ++g) {
+    float W = 0.0f, mn = INFINITY, mx = -INFINITY;
+    for (int i = 0; i < GROUP; ++i) {
+      int d = g * GROUP + i;
+      float r = k[d] - c[d];
+      W = W + w[d];
+      if (r < mn) mn = r;
+      if (r > mx) mx = r;
+    }
+    float s = f16_to_f32(f32_to_f16((mx - mn) / 3.0f));
+    E = fmaf(s * s, W, E);
+  }
+  return E;
+}
+
 /* QSAC ([QWM] 1).  Candidates: the topk smallest (weighted distance,
  * index) pairs, weighted distance acc = fma(w_d t, t, acc) with w_d t
- * rounded first.  The attention-perturbation estimate of each candidate is
- * the sensitivity-weighted squared error of its actual INT2 residual,
- * E = fold acc = fma(w_d e_d, e_d, acc) in channel order.  The lexicographic
- * minimum (E, index) is chosen. */
+ * rounded first.  The attention-perturbation estimate E of each candidate
+ * is, with score 0, the sensitivity-weighted squared error of its actual
+ * INT2 residual, E = fold acc = fma(w_d e_d, e_d, acc) in channel order;
+ * with score 1, the range-based estimate above.  The lexicographic minimum
+ * (E, index) is chosen. */
 int orc_assign_qsac(const float* k, const float* cent, int C, int D,
-                    const float* w, int topk) {
+                    const float* w, int topk, int score) {
   if (topk > C) topk = C;
   if (topk > 16) topk = 16;
   int cand[16];
@@ -263,14 +289,18 @@ int orc_assign_qsac(const float* k, const float* cent, int C, int D,
   float bestE = 0.0f;
   for (int i = 0; i < n; ++i) {
     int j = cand[i];
-    uint8_t codes[256];
-    uint32_t prm[8];
-    float e[256];
-    residual_q2(k, cent + (size_t)j * D, D, codes, prm, e);
     float E = 0.0f;
-    for (int d = 0; d < D; ++d) {
-      float we = w[d] * e[d];
-      E = fmaf(we, e[d], E);
+    if (score == 1) {
+      E = range_estimate(k, cent + (size_t)j * D, w, D);
+    } else {
+      uint8_t codes[256];
+      uint32_t prm[8];
+      float e[256];
+      residual_q2(k, cent + (size_t)j * D, D, codes, prm, e);
+      for (int d = 0; d < D; ++d) {
+        float we = w[d] * e[d];
+        E = fmaf(we, e[d], E);
+      }
     }
     if (best < 0 || E < bestE || (E == bestE && j < best)) {
       best = j;
@@ -293,11 +323,13 @@ int orc_assign_qsac(const float* k, const float* cent, int C, int D,
 /*   k_idx             u8  [B][H][Tcap]     (centroid modes)            */
 /*   centroids         f32 [B][H][C][D];  sens_w f32 [B][H][D]          */
 /*   psac_basis        f32 [B][H][D][R];  k_psac u16 [B][H][Tcap][R]     */
+/*   (INT8 coefficients: k_psac8 i8 [B][H][Tcap][R] + k_psac_sc u16       */
+/*   [B][H][Tcap], the per-token fp16 scale)                              */
 /* New tokens: k_in, v_in bf16 [B][n_new][H][D] at positions              */
 /* cur_len .. cur_len+n_new-1 of every sequence.                         */
 /* ------------------------------------------------------------------ */
 typedef struct {
-  int B, H, D, Tcap, key_mode, value_mode, C, topk, R;
+  int B, H, D, Tcap, key_mode, value_mode, C, topk, R, qsac_score, psac_fmt;
 } layout_t;
 
 static size_t bh(const layout_t* L, int b, int h) {
@@ -329,28 +361,53 @@ static void quantize_value_row(const layout_t* L, const uint16_t* v,
   }
 }
 
+/* INT8 PSAC coefficients ([QWM] 2 quantizes them to INT8): symmetric, one
+ * fp16 scale per token: sc = f16(max_m |a_m| / 127); q_m = a_m / sc
+ * rounded to the nearest integer (ties to even), clamped to [-127, 127];
+ * all zero when sc is 0.  The coefficient used is q_m * sc. */
+static void psac_int8(const float* a, int R, int8_t* q, uint16_t* sc_out) {
+  float amax = 0.0f;
+  for (int m = 0; m < R; ++m)
+    if (fabsf(a[m]) > amax) amax = fabsf(a[m]);
+  uint16_t sh = f32_to_f16(amax / 127.0f);
+  float sc = f16_to_f32(sh);
+  for (int m = 0; m < R; ++m) {
+    float v = (sc == 0.0f) ? 0.0f : rintf(a[m] / sc);
+    if (v > 127.0f) v = 127.0f;
+    if (v < -127.0f) v = -127.0f;
+    q[m] = (int8_t)v;
+  }
+  *sc_out = sh;
+}
+
 static void quantize_centroid_key(const layout_t* L, const uint16_t* kin,
                                   const float* cent, const float* w,
                                   const float* U, uint8_t* idx_out,
                                   uint8_t* code_row, uint32_t* prm,
-                                  uint16_t* psac) {
+                                  uint16_t* psac, int8_t* psac8, uint16_t* psac_sc) {
   int D = L->D;
   float k[256], e[256];
   uint8_t codes[256];
   for (int d = 0; d < D; ++d) k[d] = orc_bf16_to_f32(kin[d]);
   int j = (L->key_mode == KEY_CENTROID_QSAC)
-              ? orc_assign_qsac(k, cent, L->C, D, w, L->topk)
+              ? orc_assign_qsac(k, cent, L->C, D, w, L->topk, L->qsac_score)
               : orc_assign_plain(k, cent, L->C, D);
   residual_q2(k, cent + (size_t)j * D, D, codes, prm, e);
   orc_pack_row(codes, D, code_row);
   *idx_out = (uint8_t)j;
   /* PSAC ([QWM] 2): coefficients of the key error along the principal
-   * query directions, a_m = f16(fold acc = fma(U_dm, e_d, acc)). */
+   * query directions, a_m = fold acc = fma(U_dm, e_d, acc), stored as fp16
+   * (psac_fmt 0) or INT8 with a per-token scale (psac_fmt 1). */
+  float a[16];
   for (int m = 0; m < L->R; ++m) {
     float acc = 0.0f;
     for (int d = 0; d < D; ++d) acc = fmaf(U[(size_t)d * L->R + m], e[d], acc);
-    psac[m] = f32_to_f16(acc);
+    a[m] = acc;
   }
+  if (L->R > 0 && L->psac_fmt == 1)
+    psac_int8(a, L->R, psac8, psac_sc);
+  else
+    for (int m = 0; m < L->R; ++m) psac[m] = f32_to_f16(a[m]);
 }
 
 /* Key-range windows ([OKV]: the key quantization range is set over each
@@ -361,14 +418,15 @@ static void quantize_centroid_key(const layout_t* L, const uint16_t* kin,
  * therefore depends on the token sequence only, not on how it was split
  * into appends. */
 int orc_quantize_append(int B, int H, int D, int Tcap, int key_mode,
-                        int value_mode, int C, int topk, int R,
-                        uint8_t* k_codes, uint32_t* k_params, uint16_t* k_tail,
-                        uint8_t* k_idx, const float* centroids,
+                        int value_mode, int C, int topk, int R, int qsac_score,
+                        int psac_fmt, uint8_t* k_codes, uint32_t* k_params,
+                        uint16_t* k_tail, uint8_t* k_idx, const float* centroids,
                         const float* sens_w, const float* psac_basis,
-                        uint16_t* k_psac, uint8_t* v_codes, uint32_t* v_params,
+                        uint16_t* k_psac, int8_t* k_psac8, uint16_t* k_psac_sc,
+                        uint8_t* v_codes, uint32_t* v_params,
                         const uint16_t* k_in, const uint16_t* v_in, int cur_len,
                         int n_new) {
-  layout_t L = {B, H, D, Tcap, key_mode, value_mode, C, topk, R};
+  layout_t L = {B, H, D, Tcap, key_mode, value_mode, C, topk, R, qsac_score, psac_fmt};
   if (cur_len < 0 || n_new < 0 || cur_len + n_new > Tcap) return -3;
   const int rb = D / 4, ng = D / GROUP;
 #pragma omp parallel for collapse(2) schedule(dynamic)
@@ -418,9 +476,11 @@ int orc_quantize_append(int B, int H, int D, int Tcap, int key_mode,
           int p = cur_len + i;
           const uint16_t* kin = k_in + (((size_t)b * n_new + i) * H + h) * D;
           uint16_t* ps = (R > 0) ? k_psac + (s * Tcap + p) * R : NULL;
+          int8_t* ps8 = (R > 0) ? k_psac8 + (s * Tcap + p) * R : NULL;
+          uint16_t* psc = (R > 0) ? k_psac_sc + s * Tcap + p : NULL;
           quantize_centroid_key(&L, kin, cent, w, U, k_idx + s * Tcap + p,
                                 k_codes + (s * Tcap + p) * rb,
-                                k_params + (s * Tcap + p) * ng, ps);
+                                k_params + (s * Tcap + p) * ng, ps, ps8, psc);
         }
       }
     }
@@ -488,10 +548,12 @@ void orc_dequant_values(int H, int D, int Tcap, const uint8_t* v_codes,
 /* q f64 [B][Lq][Hq][D]; out f64 [B][Lq][Hq][D]; lse f64 [B][Hq][Lq].     */
 /* ------------------------------------------------------------------ */
 int orc_attention(int B, int H, int D, int Tcap, int key_mode, int value_mode,
-                  int C, int R, const uint8_t* k_codes, const uint32_t* k_params,
-                  const uint16_t* k_tail, const uint8_t* k_idx,
-                  const float* centroids, const float* psac_basis,
-                  const uint16_t* k_psac, const uint8_t* v_codes,
+                  int C, int R, int psac_fmt, const uint8_t* k_codes,
+                  const uint32_t* k_params, const uint16_t* k_tail,
+                  const uint8_t* k_idx, const float* centroids,
+                  const float* psac_basis, const uint16_t* k_psac,
+                  const int8_t* k_psac8, const uint16_t* k_psac_sc,
+                  const uint8_t* v_codes,
                   const uint32_t* v_params, int n, const double* q, int Lq,
                   int Hq, double scale, double* out, double* lse) {
   if (Hq % H != 0 || n < 1) return -1;
@@ -524,7 +586,10 @@ int orc_attention(int B, int H, int D, int Tcap, int key_mode, int value_mode,
             double a = 0.0;
             for (int d = 0; d < D; ++d) a += qi[d] * kh[(size_t)t * D + d];
             for (int m = 0; m < R; ++m)
-              a += qp[m] * orc_f16_to_f64(k_psac[(s * Tcap + t) * R + m]);
+              a += qp[m] * (psac_fmt == 1
+                                ? (double)k_psac8[(s * Tcap + t) * R + m] *
+                                      orc_f16_to_f64(k_psac_sc[s * Tcap + t])
+                                : orc_f16_to_f64(k_psac[(s * Tcap + t) * R + m]));
             lg[t] = scale * a;
             if (lg[t] > mx) mx = lg[t];
           }
