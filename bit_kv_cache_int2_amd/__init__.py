@@ -26,6 +26,8 @@ KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ECAPACITY, KVQ_EWORKSPACE, KVQ_EHIP = 
 KEY_WINDOW, KEY_CENTROID, KEY_CENTROID_QSAC = 0, 1, 2
 VAL_GROUP, VAL_HADAMARD = 0, 1
 F32, BF16 = 0, 1
+QSAC_EXACT, QSAC_RANGE = 0, 1     # QSAC perturbation estimate
+PSAC_F16, PSAC_INT8 = 0, 1        # PSAC coefficient storage
 GROUP, WINDOW = 32, 64
 
 BUFFERS = ("k_codes", "k_params", "k_tail", "k_idx", "centroids", "sens_w", "psac_basis",
@@ -42,7 +44,8 @@ class KVQError(RuntimeError):
 class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("batch", "kv_heads", "head_dim", "capacity",
                                                "key_mode", "value_mode", "n_centroids",
-                                               "qsac_topk", "psac_rank")]
+                                               "qsac_topk", "psac_rank", "qsac_score",
+                                               "psac_format")]
 
 
 class CacheStruct(ctypes.Structure):
@@ -116,7 +119,9 @@ class KVCache:
     [B,H,T/64,D] for window keys or [B,H,T,D/32] for centroid keys; k_tail
     i16 (bf16 bits) [B,H,64,D]; k_idx u8 [B,H,T]; centroids f32 [B,H,C,D];
     sens_w f32 [B,H,D]; psac_basis f32 [B,H,D,R]; k_psac i16 (fp16 bits)
-    [B,H,T,R]; v_codes u8 [B,H,T/64,D,16] (per 64-token tile, channel-major:
+    [B,H,T,R], or with psac_format PSAC_INT8 a u8 buffer of B*H*T*(R+2)
+    bytes viewed as k_psac8 i8 [B,H,T,R] and k_psac_sc i16 (fp16 bits)
+    [B,H,T]; v_codes u8 [B,H,T/64,D,16] (per 64-token tile, channel-major:
     token t of the tile, channel c in byte 16c + t/4, bits 2(t%4));
     v_params i32 [B,H,T,D/32].
     Calibration inputs (centroids, sens_w, psac_basis) are filled by the caller.
@@ -125,9 +130,9 @@ class KVCache:
     def __init__(self, batch: int, kv_heads: int, head_dim: int, capacity: int,
                  key_mode: int = KEY_WINDOW, value_mode: int = VAL_GROUP,
                  n_centroids: int = 0, qsac_topk: int = 1, psac_rank: int = 0,
-                 device="cuda"):
+                 qsac_score: int = QSAC_EXACT, psac_format: int = PSAC_F16, device="cuda"):
         self.layout = Layout(batch, kv_heads, head_dim, capacity, key_mode, value_mode,
-                             n_centroids, qsac_topk, psac_rank)
+                             n_centroids, qsac_topk, psac_rank, qsac_score, psac_format)
         _check(lib().kvq_layout_check(ctypes.byref(self.layout)), "layout")
         B, H, D, T = batch, kv_heads, head_dim, capacity
         shapes = {
@@ -139,7 +144,9 @@ class KVCache:
             "centroids": ((B, H, max(n_centroids, 1), D), torch.float32),
             "sens_w": ((B, H, D), torch.float32),
             "psac_basis": ((B, H, D, max(psac_rank, 1)), torch.float32),
-            "k_psac": ((B, H, T, max(psac_rank, 1)), torch.int16),
+            "k_psac": (((B * H * T * (psac_rank + 2),) if psac_format == PSAC_INT8
+                        else (B, H, T, max(psac_rank, 1))),
+                       torch.uint8 if psac_format == PSAC_INT8 else torch.int16),
             "v_codes": ((B, H, T // WINDOW, D, 16), torch.uint8),
             "v_params": ((B, H, T, D // GROUP), torch.int32),
         }
@@ -154,6 +161,11 @@ class KVCache:
             assert t.numel() * t.element_size() == nbytes, name
             setattr(self, name, t)
             self.buffers[name] = t
+        self.k_psac8 = self.k_psac_sc = None
+        if self.k_psac is not None and psac_format == PSAC_INT8:
+            n8 = B * H * T * psac_rank
+            self.k_psac8 = self.k_psac[:n8].view(torch.int8).view(B, H, T, psac_rank)
+            self.k_psac_sc = self.k_psac[n8:].view(torch.int16).view(B, H, T)
 
     def struct(self) -> CacheStruct:
         return CacheStruct(self.layout, *[_ptr(getattr(self, n)) for n in BUFFERS])

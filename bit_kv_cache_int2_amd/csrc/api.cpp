@@ -29,6 +29,11 @@ int check_layout(const kvq_layout* L) {
   if (L->key_mode == KVQ_KEY_CENTROID_QSAC &&
       (L->qsac_topk < 1 || L->qsac_topk > 8 || L->qsac_topk > L->n_centroids))
     return KVQ_EINVAL;
+  if (L->key_mode == KVQ_KEY_CENTROID_QSAC && L->qsac_score != KVQ_QSAC_EXACT &&
+      L->qsac_score != KVQ_QSAC_RANGE)
+    return KVQ_EINVAL;
+  if (L->psac_rank > 0 && L->psac_format != KVQ_PSAC_F16 && L->psac_format != KVQ_PSAC_INT8)
+    return KVQ_EINVAL;
   if ((int64_t)L->batch * L->kv_heads * L->capacity > ((int64_t)1 << 40)) return KVQ_EINVAL;
   return KVQ_OK;
 }
@@ -116,7 +121,9 @@ size_t kvq_buffer_bytes(const kvq_layout* L, int32_t which) {
     case KVQ_BUF_CENTROIDS: return BH * (size_t)L->n_centroids * D * 4;
     case KVQ_BUF_SENS_W: return BH * D * 4;
     case KVQ_BUF_PSAC_BASIS: return BH * D * (size_t)L->psac_rank * 4;
-    case KVQ_BUF_K_PSAC: return BH * T * (size_t)L->psac_rank * 2;
+    case KVQ_BUF_K_PSAC:
+      return L->psac_format == KVQ_PSAC_INT8 ? BH * T * ((size_t)L->psac_rank + 2)
+                                             : BH * T * (size_t)L->psac_rank * 2;
     default: return 0;
   }
 }

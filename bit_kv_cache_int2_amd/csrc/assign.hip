@@ -67,6 +67,51 @@ KVQ_DEV float residual_q2(const float (&k)[D], const float* __restrict__ c,
   return E;
 }
 
+// QSAC range-based estimate of candidate c ([QWM] 1: dynamic range and
+// sensitivity): sum over groups of fma(s_g * s_g, W_g), s_g the fp16 step
+// the quantizer would store for the residual group, W_g the group's summed
+// weights (fp32, channel order).
+template <int D>
+KVQ_DEV float range_estimate(const float (&k)[D], const float* __restrict__ c,
+                             const float* Wg) {
+  float E = 0.0f;
+#pragma unroll
+  for (int g = 0; g < D / kGroup; ++g) {
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < kGroup; i += 4) {
+      const float4 c4 = *reinterpret_cast<const float4*>(c + g * kGroup + i);
+      const float r0 = k[g * kGroup + i] - c4.x, r1 = k[g * kGroup + i + 1] - c4.y,
+                  r2 = k[g * kGroup + i + 2] - c4.z, r3 = k[g * kGroup + i + 3] - c4.w;
+      mn = fminf(fminf(mn, r0), fminf(fminf(r1, r2), r3));
+      mx = fmaxf(fmaxf(mx, r0), fmaxf(fmaxf(r1, r2), r3));
+    }
+    const float s = f16_bits_to_f32(f32_to_f16_bits((mx - mn) / 3.0f));
+    E = __builtin_fmaf(s * s, Wg[g], E);
+  }
+  return E;
+}
+
+// INT8 PSAC coefficients ([QWM] 2): one fp16 scale per token,
+// sc = fp16(max |a| / 127), q_m = rint(a_m / sc) clamped to [-127, 127],
+// zero when sc is 0.  Returns the scale's bits; q packed low byte first.
+template <int R>
+KVQ_DEV uint32_t psac_int8(const float (&a)[R], uint32_t (&q)[R / 4]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int m = 0; m < R; ++m) amax = fmaxf(amax, fabsf(a[m]));
+  const uint32_t sh = f32_to_f16_bits(amax / 127.0f);
+  const float sc = f16_bits_to_f32(sh);
+#pragma unroll
+  for (int m = 0; m < R / 4; ++m) q[m] = 0u;
+#pragma unroll
+  for (int m = 0; m < R; ++m) {
+    const float v = sc == 0.0f ? 0.0f : fminf(fmaxf(__builtin_rintf(a[m] / sc), -127.0f), 127.0f);
+    q[m / 4] |= ((uint32_t)(int32_t)v & 0xFFu) << (8 * (m % 4));
+  }
+  return sh;
+}
+
 // Exact squared distance of key row kr (bf16) to centroid row cr (fp32): the
 // fp32 sum in channel order with fma, t = k - c; QSAC weighs each term as
 // fma(w t, t) with w t rounded first.
@@ -157,6 +202,8 @@ constexpr int kCChunk = 64;    // centroids per LDS chunk
 constexpr int kQueue = 1024;   // per-wave rescoring queue
 constexpr int kList = 16;      // QSAC: exactly scored candidates kept per key
 constexpr float kMarginRel = 1.0f / 4096.0f;
+constexpr int kFlagRange = 1;   // QSAC: range-based perturbation estimate
+constexpr int kFlagInt8 = 2;    // PSAC: INT8 coefficients + fp16 scale
 constexpr float kMarginAbs = 1e-30f;
 
 template <int D, bool QSAC, int R, bool TO_CACHE>
@@ -166,13 +213,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     const float* __restrict__ sens_w, int topk, const float* __restrict__ basis,
     int32_t* __restrict__ idx_out, uint8_t* __restrict__ kidx,
     uint8_t* __restrict__ kcodes, uint32_t* __restrict__ kparams,
-    uint16_t* __restrict__ kpsac, int H, int Tcap, int cur_len) {
+    uint16_t* __restrict__ kpsac, int H, int Tcap, int cur_len, int flags,
+    uint16_t* __restrict__ kpsac_sc) {
+  // flags: kFlagRange = QSAC range-based estimate, kFlagInt8 = INT8 PSAC
+  // coefficients (kpsac then holds the codes, kpsac_sc the scales)
   constexpr int NKS = D / 32;
   constexpr int CP = D + 16;   // chunk row pitch (bf16): conflict-free operand reads
   __shared__ __align__(16) __bf16 chi[kCChunk * CP];
   __shared__ __align__(16) __bf16 clo[kCChunk * CP];
   __shared__ __align__(16) float cup[kCChunk], clo_[kCChunk];   // |c|^2 + Mc, |c|^2 - Mc
   __shared__ float wl[D];
+  __shared__ float wg[QSAC ? D / kGroup : 1];   // per-group weight sums
   __shared__ float ul[D * (R > 0 ? R : 1)];
   __shared__ uint32_t queue[4][kQueue];
   __shared__ int qcount[4];
@@ -206,6 +257,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
   if (lane == 0) qcount[wave] = 0;
   __syncthreads();
   if (QSAC && tid < D && !(wl[tid] >= 0.0f && wl[tid] < __builtin_inff())) bad_w = 1;
+  if (QSAC && tid < D / kGroup) {
+    float W = 0.0f;
+    for (int i = 0; i < kGroup; ++i) W = W + wl[tid * kGroup + i];
+    wg[tid] = W;
+  }
   __syncthreads();
   const bool exact_scan = (QSAC && (bad_w != 0 || topk > 4));
 
@@ -509,8 +565,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     for (int t = 0; t < kCandMax; ++t) {
       if (t < topk && t < C) {
         const int j = cj[t];
-        const float E = residual_q2<D, 0, false>(k, cb + (int64_t)j * D, wl, nullptr,
-                                                 nullptr, nullptr, nullptr);
+        const float E = (flags & kFlagRange)
+                            ? range_estimate<D>(k, cb + (int64_t)j * D, wg)
+                            : residual_q2<D, 0, false>(k, cb + (int64_t)j * D, wl, nullptr,
+                                                       nullptr, nullptr, nullptr);
         if (bestj < 0 || E < bE || (E == bE && j < bestj)) {
           bestj = j;
           bE = E;
@@ -537,6 +595,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
   uint32_t* pdst = kparams + orow * (D / kGroup);
 #pragma unroll
   for (int gq = 0; gq < D / kGroup; ++gq) pdst[gq] = prm[gq];
+  if constexpr (R > 0) {
+    if (flags & kFlagInt8) {
+      uint32_t qw[R / 4];
+      const uint32_t sh = psac_int8<R>(pacc, qw);
+      uint32_t* ps = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(kpsac) + orow * R);
+#pragma unroll
+      for (int m = 0; m < R / 4; ++m) ps[m] = qw[m];
+      kpsac_sc[orow] = (uint16_t)sh;
+      return;
+    }
+  }
   if (R > 0) {
     uint32_t hw[(R > 0 ? R : 2) / 2];
 #pragma unroll
@@ -553,11 +622,19 @@ hipError_t launch_centroid_cache(const kvq_cache* c, const void* k, int cur_len,
                                  hipStream_t st) {
   const kvq_layout& L = c->layout;
   const dim3 grid((unsigned)((n_new + 255) / 256), (unsigned)L.kv_heads, (unsigned)L.batch);
+  const bool int8 = R > 0 && L.psac_format == KVQ_PSAC_INT8;
+  const int flags = (QSAC && L.qsac_score == KVQ_QSAC_RANGE ? kFlagRange : 0) | (int8 ? kFlagInt8 : 0);
+  // INT8 coefficients: R codes per token, then the fp16 scales
+  uint16_t* psac_sc =
+      int8 ? reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(c->k_psac) +
+                                         (size_t)L.batch * L.kv_heads * L.capacity * R)
+           : nullptr;
   centroid_kernel<D, QSAC, R, true><<<grid, 256, 0, st>>>(
       (const uint16_t*)k, (int64_t)L.kv_heads * D, D, (int64_t)n_new * L.kv_heads * D, n_new,
       (const float*)c->centroids, L.n_centroids, (const float*)c->sens_w, L.qsac_topk,
       (const float*)c->psac_basis, nullptr, (uint8_t*)c->k_idx, (uint8_t*)c->k_codes,
-      (uint32_t*)c->k_params, (uint16_t*)c->k_psac, L.kv_heads, L.capacity, cur_len);
+      (uint32_t*)c->k_params, (uint16_t*)c->k_psac, L.kv_heads, L.capacity, cur_len, flags,
+      psac_sc);
   return hipGetLastError();
 }
 
@@ -567,7 +644,7 @@ hipError_t launch_assign_t(const void* keys, int64_t n, int64_t stride, const fl
   const dim3 grid((unsigned)((n + 255) / 256), 1, 1);
   centroid_kernel<D, QSAC, 0, false><<<grid, 256, 0, st>>>(
       (const uint16_t*)keys, stride, 0, 0, n, cent, C, w, topk, nullptr, out, nullptr,
-      nullptr, nullptr, nullptr, 1, 0, 0);
+      nullptr, nullptr, nullptr, 1, 0, 0, 0, nullptr);
   return hipGetLastError();
 }
 
@@ -750,7 +827,7 @@ hipError_t launch_kmeans_d(const void* keys, int B, int64_t n, int H, int64_t st
   auto assign = [&](int32_t* a) {
     centroid_kernel<D, false, 0, false><<<agrid, 256, 0, st>>>(
         (const uint16_t*)keys, stride, head_stride, batch_stride, n, cent, C, nullptr, 1,
-        nullptr, a, nullptr, nullptr, nullptr, nullptr, H, 0, 0);
+        nullptr, a, nullptr, nullptr, nullptr, nullptr, H, 0, 0, 0, nullptr);
     return hipGetLastError();
   };
   for (int it = 0; it < iters; ++it) {

@@ -58,14 +58,15 @@ struct ChunkArgs {
   const uint8_t* kidx;
   const float* cent;
   const float* basis;
-  const uint16_t* kpsac;
+  const uint16_t* kpsac;      // fp16 coefficients, or INT8 codes (psac_int8)
+  const uint16_t* kpsac_sc;   // INT8: per-token fp16 scales
   const uint8_t* vcodes;
   const uint32_t* vparams;
   const uint16_t* q;
   void* out;
   float* lse;
   float* ws;          // split partials [S][B][Lq][Hq][D + 2] when S > 1
-  int H, Hq, Tcap, C, n_tokens, Lq, out_bf16, S, tiles_per_split, n_rb;
+  int H, Hq, Tcap, C, n_tokens, Lq, out_bf16, S, tiles_per_split, n_rb, psac_int8;
   float scale_log2;
 };
 
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
   const int vc = tid >> 2, vq = tid & 3;
   const bool has_k = tid < NKT, has_v = tid < NVT;
   struct Pre {
-    uint32_t kcw, vcw, kp, vp, cf;
+    uint32_t kcw, vcw, kp, vp, cf, cs;   // cf/cs: PSAC words (INT8: two codes, scale)
     int ix;            // centroid index of token tk
     float cv[16];      // centroid channels 16 kw .. 16 kw + 15 of token tk
   };
@@ -214,10 +215,18 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
       f.ix = has_k ? (int)a.kidx[rowbase + tk] : 0;
     }
     f.cf = 0u;
-    if (R > 0 && tid < 64 * 8) {   // PSAC coefficients: two fp16 per thread
+    f.cs = 0u;
+    if (R > 0 && tid < 64 * 8) {   // PSAC coefficients: two per thread
       const int t = tid >> 3, m2 = (tid & 7) * 2;
-      if (m2 < R && t0 + t < n)
-        f.cf = reinterpret_cast<const uint32_t*>(a.kpsac + (rowbase + t) * R)[m2 / 2];
+      if (m2 < R && t0 + t < n) {
+        if (a.psac_int8) {
+          f.cf = reinterpret_cast<const uint16_t*>(
+              reinterpret_cast<const uint8_t*>(a.kpsac) + (rowbase + t) * R)[m2 / 2];
+          f.cs = a.kpsac_sc[rowbase + t];
+        } else {
+          f.cf = reinterpret_cast<const uint32_t*>(a.kpsac + (rowbase + t) * R)[m2 / 2];
+        }
+      }
     }
   };
   // centroid rows need the index, so they are requested one step later
@@ -261,7 +270,14 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
     // (stored during the previous tile) are visible
     __syncthreads();
     const int ps = tile & 1;
-    if (R > 0 && tid < 64 * 8) reinterpret_cast<uint32_t*>(coef)[(tid >> 3) * 8 + (tid & 7)] = pre.cf;
+    if (R > 0 && tid < 64 * 8) {
+      uint32_t cw = pre.cf;
+      if (a.psac_int8) {   // two INT8 codes times the token's scale, to fp16
+        const float sc = f16_bits_to_f32(pre.cs);
+        cw = pk_rne((float)(int8_t)(pre.cf & 0xFFu) * sc, (float)(int8_t)(pre.cf >> 8) * sc);
+      }
+      reinterpret_cast<uint32_t*>(coef)[(tid >> 3) * 8 + (tid & 7)] = cw;
+    }
     const uint32_t kcw = pre.kcw, vcw = pre.vcw;
     float cv[16];
 #pragma unroll
@@ -698,6 +714,11 @@ hipError_t launch_chunk(const kvq_cache* c, int n_tokens, const void* q, int q_l
   a.cent = (const float*)c->centroids;
   a.basis = (const float*)c->psac_basis;
   a.kpsac = (const uint16_t*)c->k_psac;
+  a.psac_int8 = L.key_mode != KVQ_KEY_WINDOW && L.psac_rank > 0 && L.psac_format == KVQ_PSAC_INT8;
+  a.kpsac_sc = a.psac_int8 ? reinterpret_cast<const uint16_t*>(
+                                 reinterpret_cast<const uint8_t*>(c->k_psac) +
+                                 (size_t)L.batch * L.kv_heads * L.capacity * L.psac_rank)
+                           : nullptr;
   a.vcodes = (const uint8_t*)c->v_codes;
   a.vparams = (const uint32_t*)c->v_params;
   a.q = (const uint16_t*)q;

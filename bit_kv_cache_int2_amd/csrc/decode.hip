@@ -53,12 +53,13 @@ struct DecodeArgs {
   const uint8_t* kidx;
   const float* cent;
   const float* basis;
-  const uint16_t* kpsac;
+  const uint16_t* kpsac;      // fp16 coefficients, or INT8 codes (psac_int8)
+  const uint16_t* kpsac_sc;   // INT8: per-token fp16 scales
   const uint8_t* vcodes;
   const uint32_t* vparams;
   const void* q;
   float* ws;
-  int q_bf16, H, Hq, Tcap, C, n_tokens, split_len, S;
+  int q_bf16, H, Hq, Tcap, C, n_tokens, split_len, S, psac_int8;
   float scale_log2;
 };
 
@@ -224,10 +225,13 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
 #pragma unroll
         for (int g = 0; g < G; ++g) lg[g] += qc[g][j];
         if (R > 0) {
+          // a_m: fp16, or INT8 code times the token's scale (exact in fp32)
           const uint16_t* ap = a.kpsac + tr * R;
+          const int8_t* aq = reinterpret_cast<const int8_t*>(a.kpsac) + tr * R;
+          const float sc = a.psac_int8 ? f16_bits_to_f32(a.kpsac_sc[tr]) : 0.0f;
 #pragma unroll
           for (int m = 0; m < R; ++m) {
-            const float am = f16_bits_to_f32(ap[m]);
+            const float am = a.psac_int8 ? (float)aq[m] * sc : f16_bits_to_f32(ap[m]);
 #pragma unroll
             for (int g = 0; g < G; ++g) lg[g] = __builtin_fmaf(qp[g][m], am, lg[g]);
           }
@@ -918,6 +922,11 @@ hipError_t launch_decode(const kvq_cache* c, int n_tokens, const void* q, int q_
   a.cent = (const float*)c->centroids;
   a.basis = (const float*)c->psac_basis;
   a.kpsac = (const uint16_t*)c->k_psac;
+  a.psac_int8 = L.key_mode != KVQ_KEY_WINDOW && L.psac_rank > 0 && L.psac_format == KVQ_PSAC_INT8;
+  a.kpsac_sc = a.psac_int8 ? reinterpret_cast<const uint16_t*>(
+                                 reinterpret_cast<const uint8_t*>(c->k_psac) +
+                                 (size_t)L.batch * L.kv_heads * L.capacity * L.psac_rank)
+                           : nullptr;
   a.vcodes = (const uint8_t*)c->v_codes;
   a.vparams = (const uint32_t*)c->v_params;
   a.q = q;

@@ -87,6 +87,30 @@ enum {
   KVQ_VAL_HADAMARD = 1
 };
 
+/* QSAC perturbation estimate (kvq_layout.qsac_score) */
+enum {
+  /* the candidate's actual weighted INT2 residual error, as above */
+  KVQ_QSAC_EXACT = 0,
+  /* [QWM] 1 reads as an estimate from the residual groups' dynamic range
+   * and the query sensitivity: E = sum over groups g, in order, of
+   * fma(s_g * s_g, W_g, E), s_g the fp16 step the quantizer would store for
+   * the candidate's residual group ((max - min) / 3 rounded to fp16), W_g
+   * the fp32 sum of w over the group's channels in channel order (INT2
+   * rounding noise has variance s^2/12 per element; the common 1/12 is
+   * left out).  No residual codes are needed to rank candidates. */
+  KVQ_QSAC_RANGE = 1
+};
+
+/* PSAC coefficient storage (kvq_layout.psac_format) */
+enum {
+  KVQ_PSAC_F16 = 0,   /* a_m as fp16 */
+  /* [QWM] 2 stores the coefficients as INT8: per token one fp16 scale
+   * sc = fp16(max_m |a_m| / 127) and q_m = a_m / sc rounded to nearest
+   * (ties to even), clamped to [-127, 127] (all 0 when sc is 0); the
+   * coefficient used is q_m * sc.  10 bytes per token-head instead of 16. */
+  KVQ_PSAC_INT8 = 1
+};
+
 enum { KVQ_F32 = 0, KVQ_BF16 = 1 };
 
 #define KVQ_GROUP 32  /* channels per value / residual parameter group */
@@ -104,6 +128,8 @@ typedef struct kvq_layout {
   int32_t qsac_topk;   /* QSAC candidates, 1..8 and <= C (QSAC only)   */
   int32_t psac_rank;   /* R: 0 (off) or 8 -- [QWM] 2 uses 8 directions;
                           centroid modes only                          */
+  int32_t qsac_score;  /* KVQ_QSAC_* (QSAC only; else ignored)         */
+  int32_t psac_format; /* KVQ_PSAC_* (psac_rank > 0; else ignored)     */
 } kvq_layout;
 
 /* Device buffers of one layer's packed cache.  Shapes are C order.
@@ -120,7 +146,10 @@ typedef struct kvq_layout {
  *                                      principal query directions
  *   k_psac     u16 [B][H][Tcap][R]     fp16 PSAC coefficients
  *                                      a_m = fp16(sum_d fma(U_dm, e_d)),
- *                                      e = residual - dequantised residual
+ *                                      e = residual - dequantised residual;
+ *              with KVQ_PSAC_INT8:     i8 [B][H][Tcap][R] codes q_m, then
+ *                                      u16 [B][H][Tcap] fp16 scales
+ *                                      (B*H*Tcap*(R+2) bytes in all)
  *   v_codes    u8  [B][H][Tcap/64][D][16]  value codes per 64-token tile,
  *                                      channel-major: token t of the tile,
  *                                      channel c in byte 16c + t/4, bits

@@ -24,12 +24,16 @@ def host(t: torch.Tensor, dtype) -> np.ndarray:
 def to_oracle(c: kv.KVCache) -> oracle.Cache:
     L = c.layout
     get = lambda name, dt: None if getattr(c, name) is None else np.ascontiguousarray(host(getattr(c, name), dt))
+    int8 = c.k_psac8 is not None
     return oracle.Cache(L.batch, L.kv_heads, L.head_dim, L.capacity, L.key_mode, L.value_mode,
-                        L.n_centroids, L.qsac_topk, L.psac_rank,
+                        L.n_centroids, L.qsac_topk, L.psac_rank, L.qsac_score, L.psac_format,
                         k_codes=get("k_codes", np.uint8), k_params=get("k_params", np.uint32),
                         k_tail=get("k_tail", np.uint16), k_idx=get("k_idx", np.uint8),
                         centroids=get("centroids", np.float32), sens_w=get("sens_w", np.float32),
-                        psac_basis=get("psac_basis", np.float32), k_psac=get("k_psac", np.uint16),
+                        psac_basis=get("psac_basis", np.float32),
+                        k_psac=None if int8 else get("k_psac", np.uint16),
+                        k_psac8=get("k_psac8", np.int8) if int8 else None,
+                        k_psac_sc=get("k_psac_sc", np.uint16) if int8 else None,
                         v_codes=get("v_codes", np.uint8), v_params=get("v_params", np.uint32))
 
 
@@ -37,7 +41,7 @@ def oracle_like(c: kv.KVCache) -> oracle.Cache:
     """An empty oracle cache with the same layout and calibration inputs."""
     L = c.layout
     o = oracle.Cache(L.batch, L.kv_heads, L.head_dim, L.capacity, L.key_mode, L.value_mode,
-                     L.n_centroids, L.qsac_topk, L.psac_rank)
+                     L.n_centroids, L.qsac_topk, L.psac_rank, L.qsac_score, L.psac_format)
     if c.centroids is not None:
         o.centroids[:] = host(c.centroids, np.float32)
     if c.sens_w is not None:
@@ -73,7 +77,10 @@ def assert_cache_equal(g: oracle.Cache, o: oracle.Cache, n: int, tag: str = "") 
         eq(g.k_idx[:, :, :n], o.k_idx[:, :, :n], "k_idx")
         eq(g.k_codes[:, :, :n], o.k_codes[:, :, :n], "k_codes")
         eq(g.k_params[:, :, :n], o.k_params[:, :, :n], "k_params")
-        if g.R > 0:
+        if g.R > 0 and g.psac_fmt == oracle.PSAC_INT8:
+            eq(g.k_psac8[:, :, :n], o.k_psac8[:, :, :n], "k_psac8")
+            eq(g.k_psac_sc[:, :, :n], o.k_psac_sc[:, :, :n], "k_psac_sc")
+        elif g.R > 0:
             eq(g.k_psac[:, :, :n], o.k_psac[:, :, :n], "k_psac")
 
 

@@ -37,7 +37,8 @@ def test_library_exports_every_declared_symbol():
 
 def _layout(**kw):
     d = dict(batch=2, kv_heads=4, head_dim=128, capacity=1024, key_mode=kv.KEY_WINDOW,
-             value_mode=kv.VAL_GROUP, n_centroids=0, qsac_topk=1, psac_rank=0)
+             value_mode=kv.VAL_GROUP, n_centroids=0, qsac_topk=1, psac_rank=0, qsac_score=0,
+             psac_format=0)
     d.update(kw)
     return kv.Layout(*[d[f] for f, _ in kv.Layout._fields_])
 
@@ -56,6 +57,12 @@ def test_layout_validation():
     assert chk(psac_rank=8) == kv.KVQ_EUNSUPPORTED
     assert chk(key_mode=kv.KEY_CENTROID_QSAC, n_centroids=16, qsac_topk=9) == kv.KVQ_EINVAL
     assert chk(key_mode=kv.KEY_CENTROID_QSAC, n_centroids=2, qsac_topk=4) == kv.KVQ_EINVAL
+    q = dict(key_mode=kv.KEY_CENTROID_QSAC, n_centroids=16, qsac_topk=4)
+    assert chk(**q, qsac_score=kv.QSAC_RANGE) == kv.KVQ_OK
+    assert chk(**q, qsac_score=2) == kv.KVQ_EINVAL
+    assert chk(**q, psac_rank=8, psac_format=kv.PSAC_INT8) == kv.KVQ_OK
+    assert chk(**q, psac_rank=8, psac_format=3) == kv.KVQ_EINVAL
+    assert chk(key_mode=kv.KEY_CENTROID, n_centroids=16, qsac_score=5) == kv.KVQ_OK   # ignored
 
 
 def test_buffer_sizes():
@@ -71,6 +78,10 @@ def test_buffer_sizes():
     assert nb(1) == BH * T * (D // 32) * 4
     assert nb(2) == 0 and nb(3) == BH * T and nb(4) == BH * 256 * D * 4
     assert nb(5) == BH * D * 4 and nb(6) == BH * D * 8 * 4 and nb(7) == BH * T * 8 * 2
+    # INT8 PSAC: 8 codes + one fp16 scale per token-head
+    L = _layout(key_mode=kv.KEY_CENTROID_QSAC, n_centroids=256, qsac_topk=4, psac_rank=8,
+                psac_format=kv.PSAC_INT8)
+    assert nb(7) == BH * T * 10
     assert nb(99) == 0
 
 

@@ -48,17 +48,19 @@ def test_window_chunk(T, Lq, G):
     _chunk_check(c, o, T, np.ascontiguousarray(q), f"T={T} Lq={Lq} G={G}")
 
 
-@pytest.mark.parametrize("mode,R,had", [(kv.KEY_CENTROID, 0, True), (kv.KEY_CENTROID, 0, False),
-                                        (kv.KEY_CENTROID_QSAC, 8, True)])
-def test_centroid_chunk(mode, R, had):
+@pytest.mark.parametrize("mode,R,had,fmt", [(kv.KEY_CENTROID, 0, True, 0), (kv.KEY_CENTROID, 0, False, 0),
+                                            (kv.KEY_CENTROID_QSAC, 8, True, 0),
+                                            (kv.KEY_CENTROID_QSAC, 8, True, kv.PSAC_INT8)])
+def test_centroid_chunk(mode, R, had, fmt):
     d = synth.sensitivity_aware(H=2, T=1000, Lq=200, C=64, n_cal=256)
     c = kv.KVCache(1, 2, 128, 1024, key_mode=mode, n_centroids=64, qsac_topk=4, psac_rank=R,
-                   value_mode=kv.VAL_HADAMARD if had else kv.VAL_GROUP)
+                   value_mode=kv.VAL_HADAMARD if had else kv.VAL_GROUP,
+                   qsac_score=kv.QSAC_RANGE if fmt else kv.QSAC_EXACT, psac_format=fmt)
     calibrate(c, d["K"], d["kmeans_init"], 2, d["q_cal"])
     o = oracle_like(c)
     kv.kv_quantize_append(c, dev_bf16(d["K"]), dev_bf16(d["V"]), 0)
     o.append(d["K"], d["V"], 0)
-    _chunk_check(c, o, 1000, d["q"], f"mode={mode} R={R} had={had}")
+    _chunk_check(c, o, 1000, d["q"], f"mode={mode} R={R} had={had} fmt={fmt}")
 
 
 def test_chunk_bf16_out_and_determinism():

@@ -100,12 +100,14 @@ def test_window_decode_reused_workspace():
         assert torch.equal(lse_a, lse_b), f"n={n}"
 
 
-@pytest.mark.parametrize("mode,R,had", [(kv.KEY_CENTROID, 0, True), (kv.KEY_CENTROID_QSAC, 8, True),
-                                        (kv.KEY_CENTROID_QSAC, 8, False)])
-def test_centroid_decode_psac_hadamard(mode, R, had):
+@pytest.mark.parametrize("mode,R,had,fmt", [(kv.KEY_CENTROID, 0, True, 0), (kv.KEY_CENTROID_QSAC, 8, True, 0),
+                                            (kv.KEY_CENTROID_QSAC, 8, False, 0),
+                                            (kv.KEY_CENTROID_QSAC, 8, True, kv.PSAC_INT8)])
+def test_centroid_decode_psac_hadamard(mode, R, had, fmt):
     d = synth.sensitivity_aware(H=2, T=900, Lq=4, C=32, n_cal=256)
     c = kv.KVCache(1, 2, 128, 960, key_mode=mode, n_centroids=32, qsac_topk=4, psac_rank=R,
-                   value_mode=kv.VAL_HADAMARD if had else kv.VAL_GROUP)
+                   value_mode=kv.VAL_HADAMARD if had else kv.VAL_GROUP,
+                   qsac_score=kv.QSAC_RANGE if fmt else kv.QSAC_EXACT, psac_format=fmt)
     calibrate(c, d["K"], d["kmeans_init"], 2, d["q_cal"])
     o = oracle_like(c)
     kv.kv_quantize_append(c, dev_bf16(d["K"]), dev_bf16(d["V"]), 0)
@@ -114,7 +116,7 @@ def test_centroid_decode_psac_hadamard(mode, R, had):
     qbits = np.ascontiguousarray(qbits.transpose(1, 0, 2).reshape(1, 4, 128))
     # query head 2h+g -> kv head h: heads (0,1) use q rows of kv head 0 ...
     q64 = synth.bf16_bits_to_f32(qbits).astype(np.float64)
-    _decode_check(c, o, 900, dev_bf16(qbits), q64, 1 / math.sqrt(128), f"mode={mode} R={R}")
+    _decode_check(c, o, 900, dev_bf16(qbits), q64, 1 / math.sqrt(128), f"mode={mode} R={R} fmt={fmt}")
 
 
 @pytest.mark.slow

@@ -59,16 +59,34 @@ def test_toy_centroid_keys(hadamard):
     assert_cache_equal(to_oracle(c), o, n, "toy")
 
 
-@pytest.mark.parametrize("mode,R", [(kv.KEY_CENTROID, 0), (kv.KEY_CENTROID, 8),
-                                    (kv.KEY_CENTROID_QSAC, 0), (kv.KEY_CENTROID_QSAC, 8)])
-def test_centroid_qsac_psac_hadamard(mode, R):
+@pytest.mark.parametrize("mode,R,score,fmt", [
+    (kv.KEY_CENTROID, 0, 0, 0), (kv.KEY_CENTROID, 8, 0, 0), (kv.KEY_CENTROID_QSAC, 0, 0, 0),
+    (kv.KEY_CENTROID_QSAC, 8, 0, 0),
+    # the QuantWM variants: range-based QSAC estimate, INT8 PSAC coefficients
+    (kv.KEY_CENTROID_QSAC, 0, kv.QSAC_RANGE, 0), (kv.KEY_CENTROID_QSAC, 8, kv.QSAC_RANGE, kv.PSAC_INT8),
+    (kv.KEY_CENTROID_QSAC, 8, kv.QSAC_EXACT, kv.PSAC_INT8), (kv.KEY_CENTROID, 8, 0, kv.PSAC_INT8)])
+def test_centroid_qsac_psac_hadamard(mode, R, score, fmt):
     d = synth.sensitivity_aware(H=2, T=700, Lq=8, C=32, n_cal=256)
     c = kv.KVCache(1, 2, 128, 768, key_mode=mode, value_mode=kv.VAL_HADAMARD, n_centroids=32,
-                   qsac_topk=4, psac_rank=R)
+                   qsac_topk=4, psac_rank=R, qsac_score=score, psac_format=fmt)
     calibrate(c, d["K"], d["kmeans_init"][:, :, :32], 2, d["q_cal"])
     o = oracle_like(c)
     n = _append_both(c, o, d["K"], d["V"], [300, 1, 399])
-    assert_cache_equal(to_oracle(c), o, n, f"mode={mode} R={R}")
+    assert_cache_equal(to_oracle(c), o, n, f"mode={mode} R={R} score={score} fmt={fmt}")
+
+
+def test_qsac_range_estimate_decides_differently_on_gpu():
+    """The range estimate is a different rule: on these keys some tokens pick
+    another centroid than with the exact error (both sides bit-exact)."""
+    d = synth.sensitivity_aware(H=1, T=640, Lq=8, C=32, n_cal=256)
+    idx = []
+    for score in (kv.QSAC_EXACT, kv.QSAC_RANGE):
+        c = kv.KVCache(1, 1, 128, 640, key_mode=kv.KEY_CENTROID_QSAC, n_centroids=32, qsac_topk=4,
+                       qsac_score=score)
+        calibrate(c, d["K"], d["kmeans_init"][:, :, :32], 2, d["q_cal"])
+        kv.kv_quantize_append(c, dev_bf16(d["K"]), dev_bf16(d["V"]), 0)
+        idx.append(c.k_idx.cpu().numpy())
+    assert (idx[0] != idx[1]).sum() > 0
 
 
 def test_cluster_assign_plain_and_qsac():
