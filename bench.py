@@ -318,6 +318,115 @@ def kmeans_workload(steps: int, warmup: int, with_cpu: bool = True) -> dict:
     return rec
 
 
+def variants_workload(steps: int, warmup: int) -> dict:
+    """The QuantWM variants side by side on the sensitivity-aware workload
+    (40 heads, 65,536 cached tokens, 1,560 query rows, 256 centroids fitted
+    by four kv_kmeans rounds from the seeded picks): plain centroid keys,
+    QSAC with the exact and the range-based estimate, PSAC with fp16 and
+    INT8 coefficients.  Per variant: cache bytes per token-head, append and
+    chunk-attention time, and the attention error against fp32 attention
+    over the unquantized bf16 keys and values (torch, sampled heads)."""
+    import numpy as np
+    import torch
+
+    import bit_kv_cache_int2_amd as kv
+    import synth
+
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    d = synth.sensitivity_aware()
+    H, T, Lq, C = d["Hkv"], d["T"], d["Lq"], 256
+    Tcap = ((T + 63) // 64) * 64
+    Kd, Vd, qd = to_dev(d["K"]), to_dev(d["V"]), to_dev(d["q"])
+    scale = 1.0 / math.sqrt(D)
+    # calibration inputs: centroids by GPU k-means, w and U from the calibration queries
+    K = synth.bf16_bits_to_f32(d["K"])[0]
+    cent = torch.from_numpy(np.ascontiguousarray(
+        np.stack([K[d["kmeans_init"][0, h], h] for h in range(H)])[None])).cuda()
+    kv.kv_kmeans(Kd, cent, 4)
+    del K
+    qc = synth.bf16_bits_to_f32(d["q_cal"]).astype(np.float64)
+    w = torch.from_numpy((qc ** 2).mean(0).astype(np.float32)[None]).cuda()
+    U = torch.from_numpy(np.ascontiguousarray(np.stack(
+        [np.linalg.eigh(qc[:, h].T @ qc[:, h] / qc.shape[0])[1][:, ::-1][:, :8]
+         for h in range(H)]).astype(np.float32)[None])).cuda()
+    # reference: fp32 attention over the unquantized keys and values
+    heads = (0, 13, 27, 39)
+    ref = {}
+    for h in heads:
+        q = qd[0, :, h].float()
+        k = Kd[0, :, h].float().contiguous()
+        v = Vd[0, :, h].float().contiguous()
+        p = torch.softmax((q @ k.t()) * scale, dim=-1)
+        ref[h] = p @ v
+        del p
+    torch.cuda.synchronize()
+    variants = [("centroid", kv.KEY_CENTROID, 0, kv.QSAC_EXACT, kv.PSAC_F16),
+                ("qsac_exact", kv.KEY_CENTROID_QSAC, 0, kv.QSAC_EXACT, kv.PSAC_F16),
+                ("qsac_range", kv.KEY_CENTROID_QSAC, 0, kv.QSAC_RANGE, kv.PSAC_F16),
+                ("qsac_exact+psac_f16", kv.KEY_CENTROID_QSAC, 8, kv.QSAC_EXACT, kv.PSAC_F16),
+                ("qsac_exact+psac_int8", kv.KEY_CENTROID_QSAC, 8, kv.QSAC_EXACT, kv.PSAC_INT8),
+                ("qsac_range+psac_int8", kv.KEY_CENTROID_QSAC, 8, kv.QSAC_RANGE, kv.PSAC_INT8)]
+    calib = ("centroids", "sens_w", "psac_basis")
+
+    def timed(fn, n):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(n):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e-3 / n
+
+    out = torch.empty((1, Lq, H, D), dtype=torch.float32, device="cuda")
+    table = {}
+    t0 = time.perf_counter()
+    for name, mode, R, score, fmt in variants:
+        c = kv.KVCache(1, H, D, Tcap, key_mode=mode, n_centroids=C, qsac_topk=4, psac_rank=R,
+                       value_mode=kv.VAL_HADAMARD, qsac_score=score, psac_format=fmt)
+        c.centroids.copy_(cent)
+        if c.sens_w is not None:
+            c.sens_w.copy_(w)
+        if c.psac_basis is not None:
+            c.psac_basis.copy_(U)
+        app = lambda: kv.kv_quantize_append(c, Kd, Vd, 0)
+        att = lambda: kv.attn_int2_chunk(c, T, qd, scale, out=out)
+        for _ in range(warmup):
+            app()
+            att()
+        t_app = timed(app, steps)
+        t_att = timed(att, steps)
+        err_max, num, den, abs_sum, cnt = 0.0, 0.0, 0.0, 0.0, 0
+        for h in heads:
+            dlt = out[0, :, h] - ref[h]
+            err_max = max(err_max, dlt.abs().max().item())
+            num += (dlt * dlt).sum().item()
+            den += (ref[h] * ref[h]).sum().item()
+            abs_sum += dlt.abs().sum().item()
+            cnt += dlt.numel()
+        cache_bytes = sum(t.numel() * t.element_size() for n_, t in c.buffers.items() if n_ not in calib)
+        table[name] = {"bytes_per_token_head": round(cache_bytes / (H * Tcap), 2),
+                       "compression_vs_bf16": round(512 * H * Tcap / cache_bytes, 3),
+                       "append_us": round(t_app * 1e6, 1), "chunk_us": round(t_att * 1e6, 1),
+                       "attn_err_max": float(f"{err_max:.4g}"),
+                       "attn_err_mean": float(f"{abs_sum / cnt:.4g}"),
+                       "attn_rel_l2": float(f"{math.sqrt(num / den):.4g}")}
+        del c
+        torch.cuda.empty_cache()
+    wall = time.perf_counter() - t0
+    best = table["qsac_range+psac_int8"]
+    return {"metric": "INT2 cache variants: attention rel. L2 error vs bf16 (QSAC range + INT8 PSAC)",
+            "value": best["attn_rel_l2"], "unit": "rel_l2", "n_gpus": 1, "steps": steps,
+            "warmup": warmup, "ms_per_step": round(wall / (steps * len(variants)) * 1e3, 4),
+            "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+            "data": "synthetic",
+            "config": {"workload": "variants", "heads": H, "head_dim": D, "context": T, "q_len": Lq,
+                       "centroids": "256 per head, 4 GPU k-means rounds from the seeded picks",
+                       "values": "Walsh-Hadamard rotated, int2 per token, groups of 32",
+                       "error_reference": "fp32 attention over the bf16 keys/values, heads "
+                                          + ",".join(map(str, heads)) + ", all query rows"},
+            "variants": table}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -325,7 +434,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="llm_decode",
-                    choices=["llm_decode", "long_history", "video_chunk", "sensitivity", "kmeans", "copy"])
+                    choices=["llm_decode", "long_history", "video_chunk", "sensitivity", "kmeans",
+                             "variants", "copy"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the path has no multi-GPU leg "
@@ -336,8 +446,12 @@ def main() -> int:
     if args.workload != "llm_decode":
         import torch
         torch.cuda.set_device(0)
-        run = (lambda s, w: kmeans_workload(s, w, not args.no_cpu_baseline)) if args.workload == "kmeans" \
-            else (lambda s, w: chunk_workload(args.workload, s, w))
+        if args.workload == "kmeans":
+            run = lambda s, w: kmeans_workload(s, w, not args.no_cpu_baseline)
+        elif args.workload == "variants":
+            run = variants_workload
+        else:
+            run = lambda s, w: chunk_workload(args.workload, s, w)
         print(json.dumps(run(args.steps, args.warmup)), flush=True)
         return 0
 

@@ -684,7 +684,7 @@ void orc_sens_weights(const double* q, int N, int D, float* w) {
 }
 
 /* Principal query directions ([QWM] 2): eigenvectors of the uncentred
- * second moment M = (1/N) sum q q^T ("query energy"), by cyclic Jacobi
+ * second moment M = (1/N) sum q q^T (the queries' energy), by cyclic Jacobi
  * rotations in fp64, ordered by descending eigenvalue (ties: lower original
  * index first).  Each vector's largest-magnitude component (first on ties)
  * is made positive.  U f32 [D][R] out; evals f64 [D] out (descending);
