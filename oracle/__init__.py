@@ -66,6 +66,8 @@ def lib():
     L.orc_dequant_values.restype = None
     L.orc_attention.argtypes = ([i32] * 9 + [vp] * 11 + [i32, vp, i32, i32, dbl, vp, vp])
     L.orc_attention.restype = i32
+    L.orc_top1.argtypes = [i32] * 8 + [vp] * 9 + [i32, vp, i32, i32, vp, vp]
+    L.orc_top1.restype = i32
     L.orc_merge.argtypes = [i32, i32, vp, vp, vp, vp, vp]
     L.orc_merge.restype = None
     L.orc_kmeans.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp]
@@ -304,6 +306,22 @@ class Cache:
         if rc != 0:
             raise ValueError(f"orc_attention failed: {rc}")
         return out, lse
+
+    def top1(self, q: np.ndarray, n: int):
+        """q f64 [B][Lq][Hq][D] -> (idx i32 [B][Hq][Lq], logit f64 [B][Hq][Lq]): each
+        row's largest-logit cached token (first on ties), logits before the scale."""
+        q = np.ascontiguousarray(q, np.float64)
+        B, Lq, Hq, D = q.shape
+        idx = np.empty((B, Hq, Lq), np.int32)
+        lg = np.empty((B, Hq, Lq), np.float64)
+        rc = lib().orc_top1(
+            self.B, self.H, self.D, self.Tcap, self.key_mode, max(self.C, 1), self.R, self.psac_fmt,
+            _p(self.k_codes), _p(self.k_params), _p(self.k_tail), _p(self.k_idx),
+            _p(self.centroids), _p(self.psac_basis), _p(self.k_psac), _p(self.k_psac8),
+            _p(self.k_psac_sc), int(n), _p(q), Lq, Hq, _p(idx), _p(lg))
+        if rc != 0:
+            raise ValueError(f"orc_top1 failed: {rc}")
+        return idx, lg
 
     def slice_bh(self, b: int, h: int) -> "Cache":
         """A one-sequence, one-head copy (for sampled checks at full size)."""

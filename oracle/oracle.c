@@ -616,6 +616,59 @@ int orc_attention(int B, int H, int D, int Tcap, int key_mode, int value_mode,
   return 0;
 }
 
+/* Top-1 cached token of each query row (the attention-shift diagnostic of
+ * "QuantWM: Training-Free 2-bit KV Cache Quantization for Stable Video World
+ * Models": Figure 2 and "Experimental Validation", Table 1 count how often
+ * key quantization moves a query's highest-scoring history token): the
+ * token t < n with the largest logit
+ * q.khat_t (+ (U^T q).a_t with PSAC), the same logit orc_attention uses
+ * before its scale, in fp64 over the exactly dequantised cache; the first
+ * index on ties.  idx i32 [B][Hq][Lq]; logit f64 [B][Hq][Lq]. */
+int orc_top1(int B, int H, int D, int Tcap, int key_mode, int C, int R, int psac_fmt,
+             const uint8_t* k_codes, const uint32_t* k_params, const uint16_t* k_tail,
+             const uint8_t* k_idx, const float* centroids, const float* psac_basis,
+             const uint16_t* k_psac, const int8_t* k_psac8, const uint16_t* k_psac_sc,
+             int n, const double* q, int Lq, int Hq, int32_t* idx, double* logit) {
+  if (Hq % H != 0 || n < 1) return -1;
+  const int grp = Hq / H;
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h) {
+      double* kh = (double*)malloc(sizeof(double) * (size_t)n * D);
+      if (!kh) return -2;
+      orc_dequant_keys(B, H, D, Tcap, key_mode, C, k_codes, k_params, k_tail, k_idx,
+                       centroids, b, h, n, kh);
+      size_t s = (size_t)b * H + h;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+      for (int g = 0; g < grp; ++g)
+        for (int i = 0; i < Lq; ++i) {
+          int hq = h * grp + g;
+          const double* qi = q + (((size_t)b * Lq + i) * Hq + hq) * D;
+          double qp[16] = {0};
+          for (int m = 0; m < R; ++m)
+            for (int d = 0; d < D; ++d) qp[m] += psac_basis[(s * D + d) * R + m] * qi[d];
+          int best = 0;
+          double bl = -INFINITY;
+          for (int t = 0; t < n; ++t) {
+            double a = 0.0;
+            for (int d = 0; d < D; ++d) a += qi[d] * kh[(size_t)t * D + d];
+            for (int m = 0; m < R; ++m)
+              a += qp[m] * (psac_fmt == 1
+                                ? (double)k_psac8[(s * Tcap + t) * R + m] *
+                                      orc_f16_to_f64(k_psac_sc[s * Tcap + t])
+                                : orc_f16_to_f64(k_psac[(s * Tcap + t) * R + m]));
+            if (t == 0 || a > bl) {
+              bl = a;
+              best = t;
+            }
+          }
+          idx[((size_t)b * Hq + hq) * Lq + i] = best;
+          logit[((size_t)b * Hq + hq) * Lq + i] = bl;
+        }
+      free(kh);
+    }
+  return 0;
+}
+
 /* Merge of attention partials over disjoint token sets: with partial
  * (m_s, l_s, o_s) (running max, sum of exp(logit - m_s), unnormalised
  * output) M = max m_s, l = sum exp(m_s - M) l_s,

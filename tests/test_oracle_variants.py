@@ -253,3 +253,53 @@ def test_qsac_range_cache_keys_within_bounds():
         for t in range(0, 640, 29):
             dw = _dist64(K[t, h], c.centroids[0, h], w)
             assert int(c.k_idx[0, h, t]) in np.argsort(dw, kind="stable")[:4]
+
+
+def test_top1_against_numpy_and_attention_limit():
+    """Top-1 tokens equal the numpy argmax of the compensated fp64 logits
+    over the oracle's dequantised keys, for fp16 and INT8 coefficients and
+    window keys; a very sharp softmax returns the top-1 token's value; a
+    duplicated key ties and the lower index wins."""
+    for fmt in (oracle.PSAC_F16, oracle.PSAC_INT8):
+        c, d, K = _psac_cache(fmt, T=192, H=1)
+        q = f32(d["q"])[:, :6].astype(np.float64)           # [1][6][1][D]
+        idx, lg = c.top1(q, 192)
+        U = c.psac_basis[0, 0].astype(np.float64)
+        if fmt == oracle.PSAC_F16:
+            a = oracle.f16_array_to_f64(c.k_psac[0, 0, :192])
+        else:
+            a = c.k_psac8[0, 0, :192].astype(np.float64) * oracle.f16_array_to_f64(c.k_psac_sc[0, 0, :192])[:, None]
+        Kt = c.keys(0, 0, 192) + a @ U.T
+        want = Kt @ q[0, :, 0].T                             # [T][6]
+        assert np.array_equal(idx[0, 0], np.argmax(want, axis=0))
+        assert np.allclose(lg[0, 0], want.max(0), rtol=1e-12, atol=1e-12)
+        # softmax at a huge scale picks the top-1 value (rotated back)
+        out, _ = c.attention(q, 192, 1e6)
+        import scipy.linalg
+        Hm = scipy.linalg.hadamard(128) / math.sqrt(128)
+        V = c.values(0, 0, 192)
+        for i in range(6):
+            if np.sort(want[:, i])[-1] - np.sort(want[:, i])[-2] > 1e-4:
+                assert np.allclose(out[0, i, 0], Hm @ V[idx[0, 0, i]], atol=1e-9)
+    # window keys, GQA 2
+    d = synth.llm_decode(B=1, T=128, Hq=4, Hkv=2)
+    c = oracle.Cache(1, 2, 128, 128)
+    c.append(d["K"], d["V"], 0)
+    q = f32(d["q"]).astype(np.float64)[:, None]                          # [1][1][4][D]
+    idx, lg = c.top1(q, 128)
+    for hq in range(4):
+        want = c.keys(0, hq // 2, 128) @ q[0, 0, hq]
+        assert idx[0, hq, 0] == int(np.argmax(want))
+    # an exact tie (token 70 repeats token 5; centroid keys have per-token
+    # parameters, so both dequantise alike): the lower index wins
+    Kb = np.array(d["K"][:, :, :1])
+    Kb[:, 70] = Kb[:, 5]
+    c = oracle.Cache(1, 1, 128, 128, key_mode=oracle.KEY_CENTROID, C=4)
+    c.centroids[0, 0] = f32(Kb[0, [0, 1, 2, 3], 0])
+    c.append(np.ascontiguousarray(Kb), np.ascontiguousarray(d["V"][:, :, :1]), 0)
+    kh = c.keys(0, 0, 128)
+    assert np.array_equal(kh[5], kh[70])
+    q = kh[5][None, None, None, :] * 4.0
+    idx, lg = c.top1(q, 128)
+    want = kh @ q[0, 0, 0]
+    assert want[5] == want.max() and idx[0, 0, 0] == 5
