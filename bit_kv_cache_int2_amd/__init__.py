@@ -87,6 +87,8 @@ def lib():
     L.attn_int2_chunk_workspace.restype = sz
     L.attn_int2_chunk.argtypes = [pC, i32, vp, i32, i32, ctypes.c_float, vp, i32, vp, vp, sz, vp]
     L.attn_int2_chunk.restype = ctypes.c_int
+    L.attn_int2_top1.argtypes = [pC, i32, vp, i32, i32, vp, vp, vp]
+    L.attn_int2_top1.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -266,6 +268,20 @@ def chunk_workspace(cache: KVCache, q_len: int, q_heads: int, n_tokens: int,
                     device="cuda") -> torch.Tensor:
     n = lib().attn_int2_chunk_workspace(ctypes.byref(cache.layout), q_len, q_heads, n_tokens)
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def attn_int2_top1(cache: KVCache, n_tokens: int, q: torch.Tensor, logits: bool = False,
+                   stream=None):
+    """Each query row's highest-logit cached token (q bf16 [B, Lq, Hq, D]):
+    i32 [B, Hq, Lq], and with logits=True also the f32 logits."""
+    _need_cuda(q, "q", torch.bfloat16)
+    B, Lq, Hq, D = q.shape
+    idx = torch.empty((B, Hq, Lq), dtype=torch.int32, device=q.device)
+    lg = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if logits else None
+    cs = cache.struct()
+    _check(lib().attn_int2_top1(ctypes.byref(cs), int(n_tokens), _ptr(q), Lq, Hq, _ptr(idx),
+                                _ptr(lg), _stream(stream)), "attn_int2_top1")
+    return (idx, lg) if logits else idx
 
 
 def attn_int2_chunk(cache: KVCache, n_tokens: int, q: torch.Tensor, scale: float,

@@ -25,7 +25,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 
-SOURCES = ["api.cpp", "quantize.hip", "assign.hip", "decode.hip", "chunk.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "assign.hip", "decode.hip", "chunk.hip", "top1.hip"]
 
 # Per-source extras for the attention kernels: MFMA accumulators in VGPRs
 # for decode (no copies between register files), and no NaN operands

@@ -220,6 +220,16 @@ int attn_int2_chunk(const kvq_cache* cache, int32_t n_tokens, const void* q, int
                                       out_dtype, lse, ws, (hipStream_t)stream));
 }
 
+int attn_int2_top1(const kvq_cache* cache, int32_t n_tokens, const void* q, int32_t q_len,
+                   int32_t q_heads, int32_t* idx_out, float* logit_out, void* stream) {
+  int st = check_attention(cache, n_tokens, q, q_heads, idx_out, KVQ_F32, logit_out);
+  if (st != KVQ_OK) return st;
+  if (q_len < 1) return KVQ_EINVAL;
+  if (cache->layout.batch > 65535 || q_heads > 65535) return KVQ_EUNSUPPORTED;
+  return hip_status(kvq::launch_top1(cache, n_tokens, q, q_len, q_heads, idx_out, logit_out,
+                                     (hipStream_t)stream));
+}
+
 const char* kvq_status_string(int status) {
   switch (status) {
     case KVQ_OK: return "ok";

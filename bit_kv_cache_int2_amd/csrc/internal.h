@@ -41,6 +41,9 @@ hipError_t launch_decode(const kvq_cache* c, int n_tokens, const void* q,
 size_t chunk_workspace_bytes(const kvq_layout* L, int q_len, int q_heads,
                              int n_tokens);
 
+// Top-1 cached token per query row (fp32 logits over the dequantised cache).
+hipError_t launch_top1(const kvq_cache* c, int n_tokens, const void* q, int q_len, int q_heads,
+                       int32_t* idx_out, float* logit_out, hipStream_t stream);
 hipError_t launch_chunk(const kvq_cache* c, int n_tokens, const void* q,
                         int q_len, int q_heads, float scale, void* out,
                         int out_dtype, float* lse, void* ws, hipStream_t stream);

@@ -291,6 +291,23 @@ int attn_int2_chunk(const kvq_cache* cache, int32_t n_tokens,
                     float* lse_dev, void* ws_dev, size_t ws_bytes,
                     void* stream);
 
+/* ------------------------------------------------------------ diagnostic */
+/* The attention-shift diagnostic of [QWM] (Figure 2 and "Experimental
+ * Validation", Table 1: how often key quantization moves a query's
+ * highest-scoring history token): for every query row, the cached token
+ * t < n_tokens with the largest logit q . khat_t (+ (U^T q) . a_t with
+ * PSAC), the logit attention uses before its scale; the first token on
+ * ties.  Logits in fp32: channel-order fma chains over keys dequantised per
+ * element (window: fma(code, s, z); tail: bf16; centroid: C_j + fma(code,
+ * s, z)), then the PSAC terms in order.  q_bf16_dev bf16
+ * [B][q_len][q_heads][D]; idx_out_dev i32 [B][q_heads][q_len];
+ * logit_out_dev (nullable) f32 [B][q_heads][q_len].  Not a hot path (fp32
+ * VALU, every row against every token).  Errors as attn_int2_chunk (no
+ * workspace). */
+int attn_int2_top1(const kvq_cache* cache, int32_t n_tokens, const void* q_bf16_dev,
+                   int32_t q_len, int32_t q_heads, int32_t* idx_out_dev,
+                   float* logit_out_dev, void* stream);
+
 /* Static text for a status code. */
 const char* kvq_status_string(int status);
 

@@ -126,6 +126,14 @@ def test_attention_validation_without_launch():
     assert need > 0 and need % 4 == 0
     assert L.attn_int2_chunk(ctypes.byref(c), 100, p, 0, 8, 0.1, p, kv.F32, None, p, 1 << 30,
                              None) == kv.KVQ_EINVAL
+    # the top-1 diagnostic: same cache / head / length checks, no workspace
+    top1 = lambda n=100, ql=5, hq=8, idx=p: L.attn_int2_top1(ctypes.byref(c), n, p, ql, hq, idx,
+                                                             None, None)
+    assert top1(ql=0) == kv.KVQ_EINVAL
+    assert top1(hq=6) == kv.KVQ_EINVAL
+    assert top1(n=0) == kv.KVQ_EINVAL
+    assert top1(n=2000) == kv.KVQ_ECAPACITY
+    assert top1(idx=None) == kv.KVQ_EINVAL
 
 
 def test_assign_validation_without_launch():

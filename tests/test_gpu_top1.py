@@ -1,0 +1,94 @@
+"""attn_int2_top1 (the attention-shift diagnostic) against the oracle's
+fp64 top-1 token.  The GPU forms logits in fp32, so its choice is checked
+where it is unique: the reported logit is within the fp32 error bound of the
+exact logit of the reported token, that token is within twice the bound of
+the exact maximum, and wherever the exact top-1 leads the runner-up by more
+than twice the bound the two indices agree."""
+import numpy as np
+import pytest
+import torch
+
+import bit_kv_cache_int2_amd as kv
+import oracle
+import synth
+from gpu_helpers import calibrate, dev_bf16, oracle_like, to_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _exact_logits(o: oracle.Cache, b: int, h: int, n: int, q: np.ndarray):
+    """fp64 logits [rows][n] and the sum of |terms| per (row, token)."""
+    kh = o.keys(b, h, n)
+    lg, mag = q @ kh.T, np.abs(q) @ np.abs(kh).T
+    if o.R > 0:
+        U = o.psac_basis[b, h].astype(np.float64)
+        if o.psac_fmt == oracle.PSAC_INT8:
+            a = o.k_psac8[b, h, :n].astype(np.float64) * oracle.f16_array_to_f64(o.k_psac_sc[b, h, :n])[:, None]
+        else:
+            a = oracle.f16_array_to_f64(o.k_psac[b, h, :n])
+        qp = q @ U
+        lg, mag = lg + qp @ a.T, mag + np.abs(qp) @ np.abs(a).T
+    return lg, mag
+
+
+def _check(c: kv.KVCache, n: int, qbits: np.ndarray, tag: str):
+    qd = dev_bf16(qbits)
+    idx, lg = kv.attn_int2_top1(c, n, qd, logits=True)
+    torch.cuda.synchronize()
+    idx, lg = idx.cpu().numpy(), lg.cpu().numpy()
+    o = to_oracle(c)
+    q64 = synth.bf16_bits_to_f32(qbits).astype(np.float64)      # [B][Lq][Hq][D]
+    oi, ol = o.top1(q64, n)
+    B, Lq, Hq, D = qbits.shape
+    G = Hq // o.H
+    agree = 0
+    for b in range(B):
+        for hq in range(Hq):
+            ex, mag = _exact_logits(o, b, hq // G, n, q64[b, :, hq])
+            for r in range(Lq):
+                j = int(idx[b, hq, r])
+                assert 0 <= j < n, f"{tag}: index {j}"
+                tol = 1e-5 * mag[r, j] + 1e-6
+                assert abs(lg[b, hq, r] - ex[r, j]) <= tol, f"{tag} b={b} hq={hq} r={r}: logit"
+                mx = ex[r].max()
+                assert ex[r, j] >= mx - 2 * tol - 1e-5 * mag[r].max(), f"{tag} b={b} hq={hq} r={r}: not a maximum"
+                srt = np.sort(ex[r])
+                if n == 1 or srt[-1] - srt[-2] > 2e-5 * mag[r].max() + 2e-6:
+                    assert j == oi[b, hq, r], f"{tag} b={b} hq={hq} r={r}: {j} vs {oi[b, hq, r]}"
+                    agree += 1
+                assert abs(ol[b, hq, r] - mx) < 1e-9 * max(1.0, abs(mx))
+    assert agree > 0.9 * B * Hq * Lq, f"{tag}: only {agree} unique maxima"
+
+
+@pytest.mark.parametrize("D,n,G", [(128, 1000, 1), (128, 256, 2), (64, 333, 4), (128, 1, 1)])
+def test_top1_window_keys(D, n, G):
+    d = synth.llm_decode(B=2, T=max(n, 64), Hq=2 * G, Hkv=2, D=D)
+    c = kv.KVCache(2, 2, D, ((n + 63) // 64) * 64 + 64)
+    kv.kv_quantize_append(c, dev_bf16(d["K"][:, :n]), dev_bf16(d["V"][:, :n]), 0)
+    rng = np.random.default_rng(n + D)
+    q = synth.to_bf16_bits(rng.standard_normal((2, 70, 2 * G, D)).astype(np.float32))
+    _check(c, n, q, f"window D={D} n={n} G={G}")
+
+
+@pytest.mark.parametrize("mode,R,score,fmt", [(kv.KEY_CENTROID, 0, 0, 0),
+                                              (kv.KEY_CENTROID_QSAC, 8, kv.QSAC_EXACT, kv.PSAC_F16),
+                                              (kv.KEY_CENTROID_QSAC, 8, kv.QSAC_RANGE, kv.PSAC_INT8)])
+def test_top1_centroid_psac(mode, R, score, fmt):
+    d = synth.sensitivity_aware(H=2, T=900, Lq=130, C=32, n_cal=256)
+    c = kv.KVCache(1, 2, 128, 960, key_mode=mode, n_centroids=32, qsac_topk=4, psac_rank=R,
+                   value_mode=kv.VAL_HADAMARD, qsac_score=score, psac_format=fmt)
+    calibrate(c, d["K"], d["kmeans_init"], 2, d["q_cal"])
+    kv.kv_quantize_append(c, dev_bf16(d["K"]), dev_bf16(d["V"]), 0)
+    _check(c, 900, np.ascontiguousarray(d["q"]), f"mode={mode} R={R} fmt={fmt}")
+
+
+def test_top1_validation():
+    c = kv.KVCache(1, 2, 128, 128)
+    q = torch.zeros((1, 4, 3, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(kv.KVQError):
+        kv.attn_int2_top1(c, 64, q)                 # 3 query heads over 2 kv heads
+    q = torch.zeros((1, 4, 2, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(kv.KVQError):
+        kv.attn_int2_top1(c, 0, q)
+    with pytest.raises(kv.KVQError):
+        kv.attn_int2_top1(c, 129, q)
