@@ -349,16 +349,19 @@ def variants_workload(steps: int, warmup: int) -> dict:
     U = torch.from_numpy(np.ascontiguousarray(np.stack(
         [np.linalg.eigh(qc[:, h].T @ qc[:, h] / qc.shape[0])[1][:, ::-1][:, :8]
          for h in range(H)]).astype(np.float32)[None])).cuda()
-    # reference: fp32 attention over the unquantized keys and values
+    # reference: fp32 attention over the unquantized keys and values, and each
+    # row's top-1 token (the first of the largest fp32 logit)
     heads = (0, 13, 27, 39)
-    ref = {}
+    ref, ref_top = {}, {}
     for h in heads:
         q = qd[0, :, h].float()
         k = Kd[0, :, h].float().contiguous()
         v = Vd[0, :, h].float().contiguous()
-        p = torch.softmax((q @ k.t()) * scale, dim=-1)
+        s_ = q @ k.t()
+        ref_top[h] = torch.argmax(s_, dim=-1).to(torch.int32)
+        p = torch.softmax(s_ * scale, dim=-1)
         ref[h] = p @ v
-        del p
+        del p, s_
     torch.cuda.synchronize()
     variants = [("centroid", kv.KEY_CENTROID, 0, kv.QSAC_EXACT, kv.PSAC_F16),
                 ("qsac_exact", kv.KEY_CENTROID_QSAC, 0, kv.QSAC_EXACT, kv.PSAC_F16),
@@ -395,6 +398,10 @@ def variants_workload(steps: int, warmup: int) -> dict:
             att()
         t_app = timed(app, steps)
         t_att = timed(att, steps)
+        # attention shift: rows whose top-1 cached token differs from bf16's
+        top = kv.attn_int2_top1(c, T, qd)
+        torch.cuda.synchronize()
+        shifted = sum(int((top[0, h] != ref_top[h]).sum().item()) for h in heads)
         err_max, num, den, abs_sum, cnt = 0.0, 0.0, 0.0, 0.0, 0
         for h in heads:
             dlt = out[0, :, h] - ref[h]
@@ -409,7 +416,8 @@ def variants_workload(steps: int, warmup: int) -> dict:
                        "append_us": round(t_app * 1e6, 1), "chunk_us": round(t_att * 1e6, 1),
                        "attn_err_max": float(f"{err_max:.4g}"),
                        "attn_err_mean": float(f"{abs_sum / cnt:.4g}"),
-                       "attn_rel_l2": float(f"{math.sqrt(num / den):.4g}")}
+                       "attn_rel_l2": float(f"{math.sqrt(num / den):.4g}"),
+                       "top1_shift_pct": round(100.0 * shifted / (len(heads) * Lq), 2)}
         del c
         torch.cuda.empty_cache()
     wall = time.perf_counter() - t0
@@ -423,7 +431,9 @@ def variants_workload(steps: int, warmup: int) -> dict:
                        "centroids": "256 per head, 4 GPU k-means rounds from the seeded picks",
                        "values": "Walsh-Hadamard rotated, int2 per token, groups of 32",
                        "error_reference": "fp32 attention over the bf16 keys/values, heads "
-                                          + ",".join(map(str, heads)) + ", all query rows"},
+                                          + ",".join(map(str, heads)) + ", all query rows",
+                       "top1_shift": "share of those rows whose highest-logit cached token "
+                                     "differs from the bf16 one"},
             "variants": table}
 
 
