@@ -14,12 +14,22 @@ namespace kvq {
 namespace {
 
 
+// A key row held as packed bf16 pairs (channel d in word d / 2, low half
+// first); the fp32 value is exact.
+template <int D>
+struct KeyRow {
+  uint32_t w[D / 2];
+  KVQ_DEV float operator[](int d) const {
+    return __uint_as_float((d & 1) ? (w[d >> 1] & 0xFFFF0000u) : (w[d >> 1] << 16));
+  }
+};
+
 // INT2-quantise the residual r = k - c per group of 32 (inputs
 // canonicalised), returning the weighted squared error of the dequantised
 // residual (fp32, channel order; 0 when w == nullptr).  Optionally emits the
 // packed codes, the parameter words and the PSAC accumulators.
 template <int D, int R, bool EMIT>
-KVQ_DEV float residual_q2(const float (&k)[D], const float* __restrict__ c,
+KVQ_DEV float residual_q2(const KeyRow<D>& k, const float* __restrict__ c,
                           const float* w, const float* U, uint32_t* codes,
                           uint32_t* prm, float* pacc) {
   float E = 0.0f;
@@ -72,7 +82,7 @@ KVQ_DEV float residual_q2(const float (&k)[D], const float* __restrict__ c,
 // the quantizer would store for the residual group, W_g the group's summed
 // weights (fp32, channel order).
 template <int D>
-KVQ_DEV float range_estimate(const float (&k)[D], const float* __restrict__ c,
+KVQ_DEV float range_estimate(const KeyRow<D>& k, const float* __restrict__ c,
                              const float* Wg) {
   float E = 0.0f;
 #pragma unroll
@@ -200,7 +210,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 constexpr int kCandMax = 8;    // QSAC candidates (topk <= kCandMax)
 constexpr int kCChunk = 64;    // centroids per LDS chunk
 constexpr int kQueue = 1024;   // per-wave rescoring queue
-constexpr int kList = 16;      // QSAC: exactly scored candidates kept per key
+constexpr int kList = 8;       // QSAC: candidates kept per key (more: the exact scan)
 constexpr float kMarginRel = 1.0f / 4096.0f;
 constexpr int kFlagRange = 1;   // QSAC: range-based perturbation estimate
 constexpr int kFlagInt8 = 2;    // PSAC: INT8 coefficients + fp16 scale
@@ -439,7 +449,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
   // final threshold cannot win (plain) or be in the top 4 (QSAC) and are
   // dropped.  Plain: a key with a single entry left has its winner without
   // rescoring (the winner's lower end never exceeds the final threshold);
-  // the others are rescored exactly, lanes in parallel.
+  // QSAC with topk 4: a key with exactly four entries left has its top-4
+  // set (the order inside it does not matter: the residual score decides).
+  // The others are rescored exactly, lanes in parallel.
   if (g == 0) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) thrf[wave * 64 + nt * 16 + c16] = U[nt] + 2.0f * mk[nt];
@@ -468,8 +480,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     for (int e = lane; e < cnt; e += 64) {
       const uint32_t ent = queue[wave][e];
       const int kl = (int)((ent >> 8) & 63u), j = (int)(ent & 255u);
-      if (live(ent) && (QSAC || nsurv[wave * 64 + kl] > 1)) {
-        const float dist = exact_dist<D, QSAC, true>(kb + (kbase + kl) * key_stride, cb + (int64_t)j * D, wl);
+      const int ns = nsurv[wave * 64 + kl];
+      if (live(ent) && (QSAC || ns > 1)) {
+        // QSAC: exactly topk survivors are the top-k set itself (the four
+        // smallest upper ends always survive), listed without distances
+        const float dist = (QSAC && ns == topk)
+                               ? 0.0f
+                               : exact_dist<D, QSAC, !QSAC>(kb + (kbase + kl) * key_stride,
+                                                            cb + (int64_t)j * D, wl);
         if (QSAC) {
           const int pos = atomicAdd(&ccount[wave * 64 + kl], 1);
           if (pos < kList) clist[(wave * 64 + kl) * kList + pos] = dist_key(dist, j);
@@ -488,14 +506,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
   const bool ok = i < n;
   if (!ok) return;
   const uint16_t* kr = kb + i * key_stride;
-  float k[D];
-#pragma unroll
-  for (int j = 0; j < D / 8; ++j) {
-    float x[8];
-    bf16x8_to_f32(*reinterpret_cast<const uint4*>(kr + j * 8), x);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) k[j * 8 + t] = x[t];
-  }
   int bestj = 0;
   int cj[kCandMax];
 #pragma unroll
@@ -557,6 +567,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
         bestj = j;
       }
     }
+  }
+  // the key as packed bf16 (half the registers of an fp32 row), loaded only
+  // now: the list selection and the scan above read it from memory
+  KeyRow<D> k;
+#pragma unroll
+  for (int j = 0; j < D / 8; ++j) {
+    const uint4 u = *reinterpret_cast<const uint4*>(kr + j * 8);
+    k.w[4 * j] = u.x;
+    k.w[4 * j + 1] = u.y;
+    k.w[4 * j + 2] = u.z;
+    k.w[4 * j + 3] = u.w;
   }
   if (QSAC) {
     float bE = 0.0f;
