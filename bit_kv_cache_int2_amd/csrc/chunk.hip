@@ -212,7 +212,8 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
       f.kp = (tid < D && tile < n_full) ? a.kparams[(bh * (a.Tcap / 64) + tile) * D + tid] : 0u;
     } else {
       f.kp = (tid < 64 * NG) ? a.kparams[rowbase * NG + tid] : 0u;
-      f.ix = has_k ? (int)a.kidx[rowbase + tk] : 0;
+      // rows past the length hold no index: they read centroid 0
+      f.ix = (has_k && t0 + tk < n) ? (int)a.kidx[rowbase + tk] : 0;
     }
     f.cf = 0u;
     f.cs = 0u;

@@ -63,6 +63,20 @@ def test_centroid_chunk(mode, R, had, fmt):
     _chunk_check(c, o, 1000, d["q"], f"mode={mode} R={R} had={had} fmt={fmt}")
 
 
+def test_centroid_chunk_ignores_rows_past_the_length():
+    """Index rows past the cached length are unspecified; filled with 255
+    (beyond the 32 centroids) they must change nothing in the ragged tile."""
+    d = synth.video_chunk(H=2, T=1000, Lq=70, C=32)
+    c = kv.KVCache(1, 2, 128, 1088, key_mode=kv.KEY_CENTROID, n_centroids=32,
+                   value_mode=kv.VAL_HADAMARD)
+    calibrate(c, d["K"], d["kmeans_init"], 1)
+    o = oracle_like(c)
+    kv.kv_quantize_append(c, dev_bf16(d["K"]), dev_bf16(d["V"]), 0)
+    o.append(d["K"], d["V"], 0)
+    c.k_idx[:, :, 1000:] = 255
+    _chunk_check(c, o, 1000, d["q"], "stale indices past the length", check_cache=False)
+
+
 def test_chunk_bf16_out_and_determinism():
     d = synth.video_chunk(H=2, T=700, Lq=150, C=32)
     c = kv.KVCache(1, 2, 128, 704, key_mode=kv.KEY_CENTROID, n_centroids=32,
