@@ -196,17 +196,20 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 // around its exact value.
 // A key keeps U = the smallest upper end seen so far (QSAC: at most the
 // 4th smallest, merged from the four lanes that share the key), and every
-// centroid whose lower end is at most U is rescored exactly; the winner
-// (QSAC: each of the top-4) has its lower end below the final U, so it is
-// always rescored, and the rescored set decides with the rule's own
-// arithmetic and tie order.  Rescoring goes through a per-wave queue in LDS
-// that all 64 lanes drain once the table has been seen; the best (distance, index) per key is kept by a
-// 64-bit LDS atomic min (QSAC: a list per key).  A key whose queue or list
-// overflows, weights that are negative or not finite, or topk > 4 fall back
-// to the exact scan of every centroid, lane per key.  Then, lane per key:
-// QSAC scores its top-k candidates by the INT2 residual error, and
-// TO_CACHE writes idx/codes/params/PSAC into the cache rows at cur_len + i
-// (otherwise the i32 index goes to idx_out).
+// centroid whose lower end is at most U goes to a per-wave queue in LDS
+// (with its lower end rounded down); the winner (QSAC: each of the top-4)
+// has its lower end below the final U, so it is always queued.  Once the
+// table has been seen, entries above the key's final threshold are
+// dropped; a key left with one entry (QSAC: exactly topk = 4) has its
+// answer, the others are rescored with the rule's own arithmetic and tie
+// order, all 64 lanes draining the queue together: the best (distance,
+// index) per key by a 64-bit LDS atomic min (QSAC: a list per key).  A key
+// whose queue or list overflows, weights that are negative or not finite,
+// or topk > 4 fall back to the exact scan of every centroid, lane per key.
+// Then, lane per key: QSAC scores its top-k candidates by the INT2 residual
+// error (or the range estimate), and TO_CACHE writes idx/codes/params/PSAC
+// into the cache rows at cur_len + i (otherwise the i32 index goes to
+// idx_out).
 constexpr int kCandMax = 8;    // QSAC candidates (topk <= kCandMax)
 constexpr int kCChunk = 64;    // centroids per LDS chunk
 constexpr int kQueue = 1024;   // per-wave rescoring queue
