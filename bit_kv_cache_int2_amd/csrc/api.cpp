@@ -170,6 +170,7 @@ int kv_kmeans(const void* keys, int32_t batch, int64_t n, int32_t heads, int32_t
   if (n < 0 || batch < 0 || heads < 0 || iters < 0) return KVQ_EINVAL;
   if (head_dim != 64 && head_dim != 128) return KVQ_EUNSUPPORTED;
   if (n_centroids < 1 || n_centroids > 256) return KVQ_EUNSUPPORTED;
+  if (batch > 65535 || heads > 65535) return KVQ_EUNSUPPORTED;   // grid dimensions
   if (n == 0 || batch == 0 || heads == 0) return KVQ_OK;
   if (!keys || !centroids || !aligned16(keys) || !aligned16(centroids) ||
       ((uintptr_t)assign_out & 3u))

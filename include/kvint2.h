@@ -244,7 +244,8 @@ int kv_cluster_assign(const void* keys_bf16_dev, int64_t n, int32_t head_dim,
  * assignment and the member lists of the rounds).  All work is enqueued on `stream`.  Errors:
  * KVQ_EINVAL (negative sizes or strides, iters < 0, nulls, misaligned
  * pointers, key_stride < head_dim), KVQ_EUNSUPPORTED (head_dim not 64/128,
- * n_centroids outside 1..256), KVQ_EWORKSPACE (missing or short ws). */
+ * n_centroids outside 1..256, batch or heads above 65535), KVQ_EWORKSPACE
+ * (missing or short ws). */
 size_t kv_kmeans_workspace(int32_t batch, int32_t heads, int64_t n);
 int kv_kmeans(const void* keys_bf16_dev, int32_t batch, int64_t n, int32_t heads,
               int32_t head_dim, int64_t key_stride, int64_t head_stride, int64_t batch_stride,
@@ -303,7 +304,7 @@ int attn_int2_chunk(const kvq_cache* cache, int32_t n_tokens,
  * [B][q_len][q_heads][D]; idx_out_dev i32 [B][q_heads][q_len];
  * logit_out_dev (nullable) f32 [B][q_heads][q_len].  Not a hot path (fp32
  * VALU, every row against every token).  Errors as attn_int2_chunk (no
- * workspace). */
+ * workspace), and KVQ_EUNSUPPORTED for batch or q_heads above 65535. */
 int attn_int2_top1(const kvq_cache* cache, int32_t n_tokens, const void* q_bf16_dev,
                    int32_t q_len, int32_t q_heads, int32_t* idx_out_dev,
                    float* logit_out_dev, void* stream);

@@ -167,3 +167,4 @@ def test_kmeans_validation_without_launch():
     assert call(wsb=ws - 256) == kv.KVQ_EWORKSPACE
     assert call(w=None) == kv.KVQ_EWORKSPACE
     assert call(n=0, w=None, wsb=0) == kv.KVQ_OK
+    assert call(H=70000, bs=70000 * 128 * 1000) == kv.KVQ_EUNSUPPORTED
