@@ -227,6 +227,24 @@ def test_kmeans_batched_heads_match_oracle():
 
 
 @pytest.mark.slow
+def test_kmeans_video_full_size_sampled():
+    """One Lloyd round over the video workload's keys at full size (40 heads
+    x 31,200 keys, 256 centroids, one call, as the benchmark times it):
+    sampled heads equal the oracle's k-means bit for bit."""
+    d = synth.video_chunk()
+    H, T, C = d["Hkv"], d["T"], 256
+    K = synth.bf16_bits_to_f32(d["K"])[0]                      # [T][H][D]
+    start = np.stack([K[d["kmeans_init"][0, h], h] for h in range(H)])[None]
+    cent = torch.from_numpy(np.ascontiguousarray(start)).cuda()
+    got_c, got_a = kv.kv_kmeans(dev_bf16(d["K"]), cent, 1)
+    got_c, got_a = got_c.cpu().numpy(), got_a.cpu().numpy()
+    for h in (0, 17, 39):
+        want_c, want_a = oracle.kmeans(np.ascontiguousarray(K[:, h]), C, d["kmeans_init"][0, h], 1)
+        assert np.array_equal(got_a[0, h], want_a), f"h={h}: {np.sum(got_a[0, h] != want_a)} keys differ"
+        assert np.array_equal(got_c[0, h].view(np.uint32), want_c.view(np.uint32)), f"h={h} centroids"
+
+
+@pytest.mark.slow
 def test_llm_decode_build_full_size_sampled():
     """Full 16 x 32768 x 8-head window-key build (the benchmark's launch
     configuration); all bytes of sampled (sequence, head) pairs compared."""

@@ -92,3 +92,36 @@ def test_top1_validation():
         kv.attn_int2_top1(c, 0, q)
     with pytest.raises(kv.KVQError):
         kv.attn_int2_top1(c, 129, q)
+
+
+@pytest.mark.slow
+def test_top1_video_full_size_sampled():
+    """The video workload at full size (40 heads, 31,200 cached tokens,
+    4,680 query rows, 256 centroids, one call): sampled heads and rows
+    against the oracle's top-1 over that head's dequantised cache."""
+    d = synth.video_chunk()
+    H, T, Lq = d["Hkv"], d["T"], d["Lq"]
+    c = kv.KVCache(1, H, 128, ((T + 63) // 64) * 64, key_mode=kv.KEY_CENTROID, n_centroids=256,
+                   value_mode=kv.VAL_HADAMARD)
+    calibrate(c, d["K"], d["kmeans_init"], 0)
+    kv.kv_quantize_append(c, dev_bf16(d["K"]), dev_bf16(d["V"]), 0)
+    idx, lg = kv.attn_int2_top1(c, T, dev_bf16(d["q"]), logits=True)
+    torch.cuda.synchronize()
+    idx, lg = idx.cpu().numpy(), lg.cpu().numpy()
+    g = to_oracle(c)
+    rows = sorted(set(range(0, Lq, Lq // 12)) | {Lq - 1})
+    for h in (5, 33):
+        o = g.slice_bh(0, h)
+        q64 = synth.bf16_bits_to_f32(d["q"][:, rows, h:h + 1]).astype(np.float64)
+        oi, ol = o.top1(q64, T)
+        kh = o.keys(0, 0, T)
+        for r_i, r in enumerate(rows):
+            ex = kh @ q64[0, r_i, 0]
+            mag = np.abs(kh) @ np.abs(q64[0, r_i, 0])
+            j = int(idx[0, h, r])
+            tol = 1e-5 * mag[j] + 1e-6
+            assert abs(lg[0, h, r] - ex[j]) <= tol, f"h={h} r={r}: logit"
+            assert ex[j] >= ex.max() - 2 * tol - 1e-5 * mag.max(), f"h={h} r={r}: not a maximum"
+            srt = np.sort(ex)
+            if srt[-1] - srt[-2] > 2e-5 * mag.max() + 2e-6:
+                assert j == oi[0, 0, r_i], f"h={h} r={r}: {j} vs {oi[0, 0, r_i]}"
