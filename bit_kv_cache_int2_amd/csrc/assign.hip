@@ -552,11 +552,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     for (int j = 0; j < C; ++j) {
       const float dist = exact_dist<D, QSAC>(kr, cb + (int64_t)j * D, wl);
       if (QSAC) {
+        // insertion in (distance, index) order: a displaced entry carries a
+        // lower index than the entries it may pass, so ties compare indices
         float vd = dist;
         int vj = j;
 #pragma unroll
         for (int t = 0; t < kCandMax; ++t) {
-          if (vd < cd[t]) {
+          if (vd < cd[t] || (vd == cd[t] && vj < cj[t])) {
             const float td = cd[t];
             const int tj = cj[t];
             cd[t] = vd;

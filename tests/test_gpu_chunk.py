@@ -63,6 +63,48 @@ def test_centroid_chunk(mode, R, had, fmt):
     _chunk_check(c, o, 1000, d["q"], f"mode={mode} R={R} had={had} fmt={fmt}")
 
 
+@pytest.mark.parametrize("D,C", [(64, 1), (128, 256)])
+def test_centroid_chunk_large_keys_fp16_envelope(D, C):
+    """Centroid keys far above unit rms (per-channel scales to 5, offsets of
+    sd 1.5: rms about 2.4, peaks near 20).  The chunk kernel holds each
+    dequantised centroid key as one fp16 value, the centroid plus residual
+    summed in fp32 and rounded to nearest, so its logits carry a relative
+    error of up to 2^-11 per term: against the exact attention that error
+    reaches a few 1e-3 here.  Against the exact attention over the
+    fp16-rounded keys (the same cache otherwise) it stays within the
+    tolerance, which pins the whole deviation on that one rounding."""
+    rng = np.random.default_rng(31 + D)
+    B, H, G, T, Lq = 1, 2, 2, 391, 144
+    sc = np.exp(rng.uniform(np.log(0.2), np.log(5.0), (1, 1, H, D)))
+    off = rng.normal(0, 1.5, (1, 1, H, D))
+    K = synth.to_bf16_bits((rng.standard_normal((B, T, H, D)) * sc + off).astype(np.float32))
+    V = synth.to_bf16_bits((rng.standard_normal((B, T, H, D)) * 1.5).astype(np.float32))
+    c = kv.KVCache(B, H, D, 448, key_mode=kv.KEY_CENTROID, n_centroids=C, value_mode=kv.VAL_GROUP)
+    Kf = synth.bf16_bits_to_f32(K)
+    c.centroids.copy_(torch.from_numpy(np.ascontiguousarray(
+        np.stack([[Kf[0, rng.integers(0, T, C), h] for h in range(H)]]), np.float32)))
+    kv.kv_quantize_append(c, dev_bf16(K), dev_bf16(V), 0)
+    q = synth.to_bf16_bits(rng.standard_normal((B, Lq, H * G, D)).astype(np.float32))
+    scale = 1 / math.sqrt(D)
+    out = kv.attn_int2_chunk(c, T, dev_bf16(q), scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    g = to_oracle(c)
+    q64 = synth.bf16_bits_to_f32(q).astype(np.float64)
+    exact, _ = g.attention(q64, T, scale)
+    err16 = 0.0
+    for hq in range(H * G):
+        k16 = g.keys(0, hq // G, T).astype(np.float16).astype(np.float64)
+        vh = g.values(0, hq // G, T)
+        lg = scale * q64[0, :, hq] @ k16.T
+        p = np.exp(lg - lg.max(axis=1, keepdims=True))
+        ref = (p @ vh) / p.sum(axis=1, keepdims=True)
+        err16 = max(err16, float(np.abs(got[0, :, hq] - ref).max()))
+    err = float(np.abs(got - exact).max())
+    assert err16 <= TOL, f"D={D} C={C}: {err16:.3e} from attention over fp16 keys ({err:.3e} from exact)"
+    assert err <= 8 * TOL, f"D={D} C={C}: {err:.3e} from exact attention"
+
+
 def test_centroid_chunk_ignores_rows_past_the_length():
     """Index rows past the cached length are unspecified; filled with 255
     (beyond the 32 centroids) they must change nothing in the ragged tile."""

@@ -181,6 +181,42 @@ def test_cluster_assign_exact_scan_paths():
     _assign_check(keys, cent, wn, 4, tag="negative weight")
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_exact_scan_keeps_tie_order(D):
+    """Nine copies of one centroid fill the QSAC shortlist (its capacity is
+    eight), then a strictly closer centroid arrives last: the displaced
+    copies must stay in (distance, index) order, so the lowest-index copy is
+    the one kept and chosen whenever that centroid has the smaller score.
+    Checked through kv_cluster_assign (exact score, topk 4 overflows the
+    list, topk 8 scans outright) and through the cache with both scores."""
+    rng = np.random.default_rng(14)
+    n = 600
+    A, B = rng.standard_normal((2, D)).astype(np.float32)
+    cent = np.stack([A] * 9 + [B]).astype(np.float32)
+    al = rng.uniform(0.3, 0.7, (n, 1))
+    keys = synth.to_bf16_bits((al * A + (1 - al) * B + 0.3 * rng.standard_normal((n, D))).astype(np.float32))
+    w = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    kf = synth.bf16_bits_to_f32(keys).astype(np.float64)
+    closer_b = (w * (kf - B) ** 2).sum(1) < (w * (kf - A) ** 2).sum(1) * (1 - 1e-4)
+    for topk in (4, 8):
+        got = _assign_check(keys, cent, w, topk, tag=f"tie order D={D} topk={topk}")
+        assert np.any((got == 0) & closer_b), "the construction must displace the copies"
+    for score in (kv.QSAC_EXACT, kv.QSAC_RANGE):
+        c = kv.KVCache(1, 1, D, 640, key_mode=kv.KEY_CENTROID_QSAC, n_centroids=10, qsac_topk=4,
+                       qsac_score=score)
+        c.centroids.copy_(torch.from_numpy(cent.reshape(1, 1, 10, D)))
+        c.sens_w.copy_(torch.from_numpy(w.reshape(1, 1, D)))
+        o = oracle_like(c)
+        K = np.ascontiguousarray(keys.reshape(1, n, 1, D))
+        V = synth.to_bf16_bits(rng.standard_normal((1, n, 1, D)).astype(np.float32))
+        kv.kv_quantize_append(c, dev_bf16(K), dev_bf16(V), 0)
+        o.append(K, V, 0)
+        torch.cuda.synchronize()
+        g = to_oracle(c)
+        assert_cache_equal(g, o, n, f"tie order cache D={D} score={score}")
+        assert np.any((g.k_idx[0, 0, :n] == 0) & closer_b)
+
+
 @pytest.mark.parametrize("D,C,n,iters", [(128, 64, 3000, 3), (64, 16, 512, 4), (128, 256, 4100, 2),
                                          (128, 32, 700, 0)])
 def test_kmeans_matches_oracle(D, C, n, iters):
