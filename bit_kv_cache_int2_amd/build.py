@@ -30,9 +30,12 @@ SOURCES = ["api.cpp", "quantize.hip", "assign.hip", "decode.hip", "chunk.hip", "
 # Per-source extras for the attention kernels: MFMA accumulators in VGPRs
 # for decode (no copies between register files), and no NaN operands
 # (attention never produces one from finite cache contents), which lets max
-# chains compile to v_max3_f32 without quieting each MFMA result first.
+# chains compile to v_max3_f32 without quieting each MFMA result first.  The
+# quantizer takes finite keys and values, so its min/max chains need no
+# quieting of each converted input either.
 EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
-         "chunk.hip": ["-fno-honor-nans"]}
+         "chunk.hip": ["-fno-honor-nans"],
+         "quantize.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -96,7 +96,7 @@ KVQ_DEV float range_estimate(const KeyRow<D>& k, const float* __restrict__ c,
       mn = fminf(fminf(mn, r0), fminf(fminf(r1, r2), r3));
       mx = fmaxf(fmaxf(mx, r0), fmaxf(fmaxf(r1, r2), r3));
     }
-    const float s = f16_bits_to_f32(f32_to_f16_bits((mx - mn) / 3.0f));
+    const float s = f16_bits_to_f32(f32_to_f16_bits(div3(mx - mn)));
     E = __builtin_fmaf(s * s, Wg[g], E);
   }
   return E;

@@ -58,6 +58,17 @@ KVQ_DEV void bf16x8_to_f32(const uint4 u, float* x) {
   }
 }
 
+// (mx - mn) / 3 correctly rounded in four operations: q0 = d * RN(1/3), the
+// exact residual r = d - 3 q0 by fma, then q0 + r * RN(1/3) rounded once.
+// Equal to the division for every non-negative fp32 d (checked over all of
+// them); d = +inf gives NaN there, which the final min turns back into +inf.
+KVQ_DEV float div3(float d) {
+  const float y = 0x1.555556p-2f;
+  const float q0 = d * y;
+  const float r = __builtin_fmaf(-3.0f, q0, d);
+  return fminf(__builtin_fmaf(r, y, q0), d);
+}
+
 // The INT2 group quantizer's parameters for a group with extrema mn, mx
 // (canonical inputs).  t0..t2 are the three decision thresholds; when the
 // stored scale is 0 they are +inf so that every code is 0.
@@ -72,7 +83,7 @@ KVQ_DEV Q2 q2_make(float mn, float mx) {
   Q2 q;
   mn = mn + 0.0f;
   mx = mx + 0.0f;
-  const float s32 = (mx - mn) / 3.0f;
+  const float s32 = div3(mx - mn);
   const uint32_t sh = f32_to_f16_bits(s32), zh = f32_to_f16_bits(mn);
   q.s = f16_bits_to_f32(sh);
   q.z = f16_bits_to_f32(zh);

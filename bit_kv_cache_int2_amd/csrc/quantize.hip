@@ -14,6 +14,36 @@
 namespace kvq {
 namespace {
 
+
+// INT2 codes by sign bits.  The kernels hold each threshold negated,
+// u_k = fma(-(k + 1/2), s, -z) = -t_k exactly, which is +0 (never -0) when
+// t_k is zero and -inf for a zero step.  The sign of RN(x + u_k) is then the
+// sign of the exact x - t_k, so bit 31 of x + u_k is (x < t_k), zeros
+// included.  With s_k = (x < t_k) and t0 <= t1 <= t2, the code's high bit is
+// not s1 and its low bit is not (s1 ? s0 : s2): the middle threshold picks
+// the outer one.  acc collects the inverted bits from the top element down,
+// one v_alignbit (acc << 1 | d >> 31) per bit, starting from all ones so
+// that the inverted word has zeros above the bits collected.
+struct NegThr {
+  float u0, u1, u2;
+};
+
+KVQ_DEV NegThr neg_thresholds(const Q2& q) {
+  NegThr n;
+  const bool zero = (q.s == 0.0f);
+  n.u0 = zero ? -__builtin_inff() : __builtin_fmaf(-0.5f, q.s, -q.z);
+  n.u1 = zero ? -__builtin_inff() : __builtin_fmaf(-1.5f, q.s, -q.z);
+  n.u2 = zero ? -__builtin_inff() : __builtin_fmaf(-2.5f, q.s, -q.z);
+  return n;
+}
+
+KVQ_DEV uint32_t code_bits(uint32_t acc, float x, float u0, float u1, float u2) {
+  const uint32_t d0 = __float_as_uint(x + u0), d1 = __float_as_uint(x + u1),
+                 d2 = __float_as_uint(x + u2);
+  acc = __builtin_amdgcn_alignbit(acc, d1, 31);
+  return __builtin_amdgcn_alignbit(acc, (d1 & d0) | (~d1 & d2), 31);   // v_bfi_b32
+}
+
 // ---------------------------------------------------------------- values
 // Walsh-Hadamard rotation of one token row spread over D/8 lanes (8
 // elements per lane, element index = lane-in-row * 8 + k).  Stages run with
@@ -71,7 +101,7 @@ __global__ __launch_bounds__(256) void tile_append_kernel(
     uint32_t* __restrict__ vparams, int H, int Tcap, int cur_len, int n_new) {
   constexpr int LPR = D / 8, RPP = 256 / LPR, NP = kWindow / RPP;
   __shared__ float red_mn[4][D], red_mx[4][D];
-  __shared__ float thr[3][D];
+  __shared__ float thr[3][D];   // negated key thresholds per channel
   __shared__ __align__(16) uint32_t vt[D][4];
 
   // heads vary fastest across blocks: the heads of one token are adjacent
@@ -88,18 +118,24 @@ __global__ __launch_bounds__(256) void tile_append_kernel(
   const uint16_t* tail = ktail + bh * kWindow * D;
   uint32_t* vtile = reinterpret_cast<uint32_t*>(vcodes + (bh * (Tcap / kWindow) + w) * (int64_t)D * 16);
 
+  // Every load is issued unconditionally from an in-bounds row (a guarded
+  // load compiles to a branch around a wait, which would serialise them):
+  // value rows clamp into the new tokens [t_lo, t_hi); key rows read the
+  // window when it completes (earlier tokens from the tail) and otherwise
+  // the same clamped rows, whose contents go unused.  Rows outside
+  // [t_lo, t_hi) give codes in tile slots past the stream's end, which are
+  // unspecified, or none at all.
+  const int64_t row0 = ((int64_t)b * n_new - cur_len) * H + h;   // row index of token p: row0 + p * H
   uint4 vraw[NP], kraw[NP];
 #pragma unroll
   for (int k = 0; k < NP; ++k) {
     const int p = wb + r0 + RPP * k;
-    const bool vok = p >= t_lo && p < t_hi;
-    vraw[k] = vok ? ld_stream(vin + (((int64_t)b * n_new + (p - cur_len)) * H + h) * D + j * 8)
-                  : make_uint4(0u, 0u, 0u, 0u);
-    if (full) {
-      const uint16_t* src = (p < cur_len) ? tail + (int64_t)(p & (kWindow - 1)) * D
-                                          : kin + (((int64_t)b * n_new + (p - cur_len)) * H + h) * D;
-      kraw[k] = ld_stream(src + j * 8);
-    }
+    const int pc = min(max(p, t_lo), t_hi - 1);
+    vraw[k] = ld_stream(vin + (row0 + (int64_t)pc * H) * D + j * 8);
+    const int pk = full ? p : pc;
+    const uint16_t* src = (pk < cur_len) ? tail + (int64_t)(pk & (kWindow - 1)) * D
+                                         : kin + (row0 + (int64_t)pk * H) * D;
+    kraw[k] = ld_stream(src + j * 8);
   }
   // value tile words.  A tile that starts fresh (no earlier tokens in it) is
   // assembled from whole bytes; otherwise the words start from the codes of
@@ -136,9 +172,11 @@ __global__ __launch_bounds__(256) void tile_append_kernel(
     mn = fminf(mn, __shfl_xor(mn, 2, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
     const Q2 q = q2_make(mn, mx);
-    uint32_t bits = 0;                       // channel 8j+e at bits [2e, 2e+1]
+    const NegThr u = neg_thresholds(q);
+    uint32_t acc = ~0u;                      // channel 8j+e at bits [2e, 2e+1] of ~acc
 #pragma unroll
-    for (int e = 0; e < 8; ++e) bits |= q2_code(x[e], q) << (2 * e);
+    for (int e = 7; e >= 0; --e) acc = code_bits(acc, x[e], u.u0, u.u1, u.u2);
+    const uint32_t bits = ~acc & 0xFFFFu;
     if (fresh) {
       // D = 128: lanes 16i + j (i = 0..3) of this wave hold tokens 4*wave + i
       // (+16k) of the same 8 channels.  Spread each lane's codes to one byte
@@ -211,28 +249,26 @@ __global__ __launch_bounds__(256) void tile_append_kernel(
         c = fmaxf(c, red_mx[v][tid]);
       }
       const Q2 q = q2_make(a, c);
-      thr[0][tid] = q.t0;
-      thr[1][tid] = q.t1;
-      thr[2][tid] = q.t2;
+      const NegThr u = neg_thresholds(q);
+      thr[0][tid] = u.u0;
+      thr[1][tid] = u.u1;
+      thr[2][tid] = u.u2;
       kparams[(bh * (Tcap / kWindow) + w) * D + tid] = q.word;
     }
     __syncthreads();
-    float t0[8], t1[8], t2[8];
+    float u0[8], u1[8], u2[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      t0[e] = thr[0][j * 8 + e];
-      t1[e] = thr[1][j * 8 + e];
-      t2[e] = thr[2][j * 8 + e];
+      u0[e] = thr[0][j * 8 + e];
+      u1[e] = thr[1][j * 8 + e];
+      u2[e] = thr[2][j * 8 + e];
     }
 #pragma unroll
     for (int k = 0; k < NP; ++k) {
-      uint32_t bits = 0;
+      uint32_t acc = ~0u;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = kx[k][e];
-        const bool up = x >= t1[e];   // ordered thresholds: see q2_code
-        bits |= ((up ? 2u : 0u) + (uint32_t)(x >= (up ? t2[e] : t0[e]))) << (2 * e);
-      }
+      for (int e = 7; e >= 0; --e) acc = code_bits(acc, kx[k][e], u0[e], u1[e], u2[e]);
+      const uint32_t bits = ~acc;
       *reinterpret_cast<uint16_t*>(kcodes + (bh * Tcap + wb + r0 + RPP * k) * (D / 4) + j * 2) =
           (uint16_t)bits;
     }

@@ -200,6 +200,8 @@ int kvq_layout_check(const kvq_layout* L);
 /* Quantise tokens [cur_len, cur_len + n_new) of every sequence into the
  * cache ([QWM] 1 and 2, [OKV] windows and rotated values).
  * k_bf16_dev, v_bf16_dev: bf16 [B][n_new][H][D] (the new tokens).
+ * Keys and values must be finite: a NaN or an infinity gives unspecified
+ * codes and parameters for its group.
  * Window keys: every window completed by this append is quantised per
  * channel from the tail and the new tokens; the tokens of the window left
  * unfinished are written to the tail.  The cache bytes depend on the token
