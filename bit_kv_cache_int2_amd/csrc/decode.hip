@@ -27,6 +27,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Most windows one split (one block) covers: eight per wave.
 constexpr int kDecodeMaxWindows = 32;
+constexpr double kBlockOverheadWindows = 16.0;   // see decode_splits
 // Resident blocks per CU of the MFMA decode kernel (LDS and register use
 // are sized for three).
 constexpr int kDecodeBlocksPerCU = 3;
@@ -870,9 +871,15 @@ hipError_t launch_partial_g(const DecodeArgs& a, int G, int key_mode, int R, int
 }  // namespace
 
 // Splits per (sequence, kv head).  A split covers at most
-// kDecodeMaxWindows windows; among the admissible counts the one that fills
-// the device's resident block slots in the fewest, fullest rounds wins
-// (cost = rounds x (windows per split + 2 windows of per-block overhead)).
+// kDecodeMaxWindows windows.  Each block costs its windows plus a fixed
+// overhead (pipeline fill and drain, the 4-wave merge, its share of the
+// split merge) worth about kBlockOverheadWindows windows, and blocks beyond
+// the device's resident slots queue behind the others: cost = max(1, blocks
+// / slots) x (windows per split + kBlockOverheadWindows).  On the LLM decode
+// workload (16 x 8 heads x 512 windows) decode time against the split count
+// follows that cost with an overhead of 16 to 18 windows (16 splits: 80 us,
+// 18: 86 us, 24: 93 us, 32: 107 us, 64: 167 us), so long splits win once the
+// device is full and more splits only help while it is not.
 int decode_splits(const kvq_layout* L, int q_heads, int n_tokens) {
   (void)q_heads;
   const int n_win = (n_tokens + kWindow - 1) / kWindow;
@@ -892,8 +899,8 @@ int decode_splits(const kvq_layout* L, int q_heads, int n_tokens) {
   for (int S = s_min; S <= s_max; ++S) {
     const int per = (n_win + S - 1) / S;
     if ((n_win + per - 1) / per != S) continue;     // same partition as a smaller S
-    const double rounds = (double)((units * S + slots - 1) / slots);
-    const double cost = rounds * (per + 2.0);
+    const double fill = (double)(units * S) / (double)slots;
+    const double cost = (fill > 1.0 ? fill : 1.0) * (per + kBlockOverheadWindows);
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best = S;
