@@ -36,7 +36,11 @@ constexpr int kDecodeBlocksPerCU = 3;
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kNT = 2;
 // Prefetch distances (windows) of the MFMA decode's key and value streams.
+// Pass 1 requests the first value windows during its last kKeyAhead steps
+// and pass 2 requests window k + kValAhead at its step k, so every value
+// window is requested exactly once only while kValAhead <= kKeyAhead.
 constexpr int kKeyAhead = 3, kValAhead = 3;
+static_assert(kValAhead <= kKeyAhead, "value windows kKeyAhead..kValAhead-1 would never be loaded");
 
 // Orders one wave's LDS writes before its following LDS reads (data shared
 // between lanes of a wave).  The fences are restricted to LDS ("local"), so
