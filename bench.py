@@ -43,7 +43,7 @@ if ROOT not in sys.path:
 METRIC = "INT2 decode-attn effective GB/s & %HBM peak; quantize-append Mtok/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 B, HQ, HKV, D, T = 16, 32, 8, 128, 32768
-CPU_SAMPLE_SEQS = 4            # oracle timed on 4 of the 16 sequences
+CPU_SAMPLE_SEQS = 16          # the whole workload: about 9 s of oracle work on the 16 host threads
 
 # Algorithmic bytes per step (what the method must move, not what a kernel
 # happens to move): the append reads bf16 K and V and writes codes and
@@ -114,9 +114,9 @@ def copy_calibration(steps: int) -> int:
 
 
 def cpu_baseline(d) -> dict:
-    """The oracle as it stands, on a bounded sample: the first
-    CPU_SAMPLE_SEQS sequences (all 8 KV heads, all 32768 tokens): append,
-    then fp64 attention for their 32 query heads."""
+    """The oracle as it stands, on the first CPU_SAMPLE_SEQS sequences (all
+    8 KV heads, all 32768 tokens; by default all 16, the whole workload):
+    append, then fp64 attention for their 32 query heads."""
     import numpy as np
 
     import oracle
