@@ -610,27 +610,40 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(const DecodeArgs a)
   float M[G];
   float l_lane[G], pz[G][4];
   f4 o[8], ocorr;
-  // bases of the value operand: dword j of k-step k2 holds the tokens of
-  // code-word positions i = 4 k2 + j and i + 8
+  // The value operand of token t is base + c (c the code); the P~ operand
+  // rounds p s once per (token, group).  The output removes (base + 3/2)
+  // per token through the vbase MFMA and adds z + 3/2 s through pz, so
+  // what P~'s rounding multiplies is s (c - 3/2), which has both signs
+  // within a group.  (Removing only the base would leave s c, of one sign,
+  // and an inverse rotation gathers such same-signed errors into one
+  // output channel: 2.0e-3 instead of 2.5e-4 on a rotated cache with value
+  // ranges near 9.)  base + 3/2 is exact in fp16.
+  // Dword j of k-step k2 holds the tokens of code-word positions
+  // i = 4 k2 + j and i + 8.
   h8 vbase[2];
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) vbase[k2][j] = (_Float16)code_base(4 * k2 + j / 2);
+    for (int j = 0; j < 8; ++j) vbase[k2][j] = (_Float16)(code_base(4 * k2 + j / 2) + 1.5f);
   // P~ -> LDS in the operand's token order: token 16 gk + o pairs with
   // o + 8; k index 2 i' + (o >= 8) of k-step (o % 8) / 4
   const int kk = (c16 & 7) >> 2, jj = 2 * (c16 & 3) + (c16 >> 3);
   auto window_pv = [&](const VWin& cur, int slot) {
     const uint32_t vw[4] = {cur.vp.x, cur.vp.y, cur.vp.z, cur.vp.w};
+    float sc[4], zc[4];   // group scale, and zero + 3/2 scale (see vbase)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      sc[q] = f16_bits_to_f32(vw[q]);
+      zc[q] = __builtin_fmaf(1.5f, sc[q], f16_bits_to_f32(vw[q] >> 16));
+    }
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       const float p = __builtin_amdgcn_exp2f(sl[wave][slot][hh][lane ^ (16 * hh)] - M[hh]);
       l_lane[hh] += p;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float sc = f16_bits_to_f32(vw[q]), zc = f16_bits_to_f32(vw[q] >> 16);
-        pz[hh][q] = __builtin_fmaf(p, zc, pz[hh][q]);
-        pb[wave][4 * q + hh][g * 16 + kk * 8 + jj] = (_Float16)(p * sc);
+        pz[hh][q] = __builtin_fmaf(p, zc[q], pz[hh][q]);
+        pb[wave][4 * q + hh][g * 16 + kk * 8 + jj] = (_Float16)(p * sc[q]);
       }
     }
     wave_lds_sync();

@@ -21,7 +21,7 @@ from gpu_helpers import TOL, assert_cache_equal, dev_bf16, oracle_like, to_oracl
 
 pytestmark = pytest.mark.gpu
 
-CASES = 24
+CASES = 96
 
 
 def _draw(case: int):
