@@ -9,6 +9,7 @@ dropped from the list: case 13 (nine copies of a centroid in a 256-entry
 table overflowing the QSAC shortlist) is the tie-order regression of the
 exact scan."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -21,7 +22,7 @@ from gpu_helpers import TOL, assert_cache_equal, dev_bf16, oracle_like, to_oracl
 
 pytestmark = pytest.mark.gpu
 
-CASES = 96
+CASES = int(os.environ.get("KVQ_SWEEP_CASES", "300"))   # more for a deeper one-off sweep
 
 
 def _draw(case: int):
