@@ -25,11 +25,11 @@ pytestmark = pytest.mark.gpu
 CASES = int(os.environ.get("KVQ_SWEEP_CASES", "300"))   # more for a deeper one-off sweep
 
 
-def _draw(case: int):
-    r = np.random.default_rng(9000 + case)
+def _draw(case: int, seed0: int = 9000, t_range=(1, 700), lq_range=(1, 150), g_choices=(1, 2, 4)):
+    r = np.random.default_rng(seed0 + case)
     cfg = dict(D=int(r.choice([64, 128])), key_mode=int(r.integers(0, 3)),
                value_mode=int(r.integers(0, 2)), B=int(r.integers(1, 3)), H=int(r.integers(1, 4)),
-               G=int(r.choice([1, 2, 4])), T=int(r.integers(1, 700)))
+               G=int(r.choice(list(g_choices))), T=int(r.integers(*t_range)))
     cfg["cap_extra"] = int(r.integers(0, 2)) * 64
     centroid = cfg["key_mode"] != kv.KEY_WINDOW
     cfg["C"] = int(r.choice([1, 5, 32, 256])) if centroid else 0
@@ -40,17 +40,30 @@ def _draw(case: int):
     cuts = sorted(r.choice(np.arange(1, cfg["T"]), size=min(int(r.integers(0, 3)), cfg["T"] - 1), replace=False)) \
         if cfg["T"] > 1 else []
     cfg["chunks"] = [int(x) for x in np.diff([0] + [int(x) for x in cuts] + [cfg["T"]])]
-    cfg["Lq"] = int(r.integers(1, 150))
+    cfg["Lq"] = int(r.integers(*lq_range))
     cfg["q_f32"] = bool(r.random() < 0.5)
     return cfg, r
 
 
 @pytest.mark.parametrize("case", range(CASES))
 def test_random_configuration(case):
-    cfg, r = _draw(case)
+    _run(*_draw(case), f"case {case}")
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_long_configuration(case):
+    """Longer caches (700 to 6,000 tokens) and 100 to 600 query rows: decode
+    over many token splits and chunk attention over several row blocks and
+    token splits, so the split merges see random shapes too.  Chunk rows are
+    sampled (every fifth row and the last) to bound the oracle's time."""
+    cfg, r = _draw(case, seed0=19000, t_range=(700, 6000), lq_range=(100, 600), g_choices=(1, 2, 4, 8))
+    _run(cfg, r, f"long case {case}", chunk_rows=slice(None, None, 5))
+
+
+def _run(cfg, r, name, chunk_rows=None):
     D, B, H, T, G = cfg["D"], cfg["B"], cfg["H"], cfg["T"], cfg["G"]
     Hq = H * G
-    tag = f"case {case}: {cfg}"
+    tag = f"{name}: {cfg}"
     # keys: per-channel scales and offsets (window ranges and residuals both
     # see spread).  Window keys take a wide spread (rms about 2.4, peaks near
     # 20); centroid keys stay near the unit rms of the centroid workloads,
@@ -107,6 +120,7 @@ def test_random_configuration(case):
     qc = synth.to_bf16_bits(r.standard_normal((B, Lq, Hq, D)).astype(np.float32))
     outc = kv.attn_int2_chunk(c, T, dev_bf16(qc), scale)
     torch.cuda.synchronize()
-    refc, _ = g.attention(synth.bf16_bits_to_f32(qc).astype(np.float64), T, scale)
-    errc = np.abs(outc.cpu().numpy().astype(np.float64) - refc)
+    rows = np.arange(Lq) if chunk_rows is None else np.unique(np.r_[np.arange(Lq)[chunk_rows], Lq - 1])
+    refc, _ = g.attention(np.ascontiguousarray(synth.bf16_bits_to_f32(qc[:, rows]).astype(np.float64)), T, scale)
+    errc = np.abs(outc.cpu().numpy()[:, rows].astype(np.float64) - refc)
     assert np.all(errc <= TOL), f"{tag}: chunk max err {errc.max():.3e}"
