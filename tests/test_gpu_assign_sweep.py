@@ -67,3 +67,39 @@ def test_random_assignment(case):
     assert bad.size == 0, (f"case {case} (C={len(cent)}, D={cent.shape[1]}, n={len(kb)}, topk={topk}, "
                            f"qsac={w is not None}): {bad.size} differ, first {bad[:5]} got {got[bad[:5]]} "
                            f"want {want[bad[:5]]}")
+
+
+def _draw_kmeans(case: int):
+    r = np.random.default_rng(41000 + case)
+    D = int(r.choice([64, 128]))
+    B, H = int(r.integers(1, 3)), int(r.integers(1, 4))
+    n = int(r.integers(1, 2500))
+    C = int(r.integers(1, min(256, n) + 1))
+    iters = int(r.integers(0, 4))
+    scale = float(np.exp(r.uniform(np.log(1e-2), np.log(1e2))))
+    centers = scale * r.standard_normal((max(C // 2, 1), D))
+    keys = centers[r.integers(0, len(centers), (B, n, H))] + 0.6 * scale * r.standard_normal((B, n, H, D))
+    kb = synth.to_bf16_bits(keys.astype(np.float32))
+    init = np.stack([np.stack([r.choice(n, C, replace=False) for _ in range(H)]) for _ in range(B)])
+    if C > 2 and r.random() < 0.5:          # a duplicated starting pick: one cluster stays empty
+        init[:, :, C - 1] = init[:, :, 0]
+    return kb, init, C, iters
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_random_kmeans(case):
+    """kv_kmeans over random batches, heads, key counts, centroid counts
+    (with empty clusters) and round counts: every (sequence, head) table and
+    its last assignment equal the oracle's Lloyd rounds bit for bit."""
+    kb, init, C, iters = _draw_kmeans(case)
+    B, n, H, D = kb.shape
+    kf = synth.bf16_bits_to_f32(kb)
+    start = np.stack([np.stack([kf[b, init[b, h], h] for h in range(H)]) for b in range(B)])
+    got_c, got_a = kv.kv_kmeans(dev_bf16(kb), torch.from_numpy(np.ascontiguousarray(start)).cuda(), iters)
+    got_c, got_a = got_c.cpu().numpy(), got_a.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            want_c, want_a = oracle.kmeans(np.ascontiguousarray(kf[b, :, h]), C, init[b, h], iters)
+            tag = f"case {case} (B={B}, n={n}, H={H}, D={D}, C={C}, iters={iters}) b={b} h={h}"
+            assert np.array_equal(got_a[b, h], want_a), f"{tag}: assignment"
+            assert np.array_equal(got_c[b, h].view(np.uint32), want_c.view(np.uint32)), f"{tag}: centroids"
