@@ -125,3 +125,33 @@ def test_top1_video_full_size_sampled():
             srt = np.sort(ex)
             if srt[-1] - srt[-2] > 2e-5 * mag.max() + 2e-6:
                 assert j == oi[0, 0, r_i], f"h={h} r={r}: {j} vs {oi[0, 0, r_i]}"
+
+
+@pytest.mark.parametrize("case", range(20))
+def test_top1_random_configuration(case):
+    """Seeded random layouts (key mode, head_dim, PSAC off / fp16 / INT8,
+    batch, heads, GQA, cached length, query rows) through the same checks."""
+    r = np.random.default_rng(52000 + case)
+    D = int(r.choice([64, 128]))
+    mode = int(r.integers(0, 3))
+    B, H, G = int(r.integers(1, 3)), int(r.integers(1, 4)), int(r.choice([1, 2, 4]))
+    n, Lq = int(r.integers(1, 1500)), int(r.integers(1, 150))
+    C = int(r.choice([1, 8, 64])) if mode != kv.KEY_WINDOW else 0
+    R = 8 if mode != kv.KEY_WINDOW and r.random() < 0.5 else 0
+    fmt = kv.PSAC_INT8 if R and r.random() < 0.5 else kv.PSAC_F16
+    K = synth.to_bf16_bits((r.standard_normal((B, n, H, D)) * r.uniform(0.5, 2.0, (1, 1, H, D))).astype(np.float32))
+    V = synth.to_bf16_bits(r.standard_normal((B, n, H, D)).astype(np.float32))
+    c = kv.KVCache(B, H, D, ((n + 63) // 64) * 64, key_mode=mode, n_centroids=C,
+                   qsac_topk=min(4, C) if mode == kv.KEY_CENTROID_QSAC else 1, psac_rank=R, psac_format=fmt)
+    if c.centroids is not None:
+        Kf = synth.bf16_bits_to_f32(K)
+        cent = np.stack([np.stack([Kf[b, r.integers(0, n, C), h] for h in range(H)]) for b in range(B)])
+        c.centroids.copy_(torch.from_numpy(np.ascontiguousarray(cent, np.float32)))
+    if c.sens_w is not None:
+        c.sens_w.copy_(torch.from_numpy(r.uniform(0.1, 3.0, (B, H, D)).astype(np.float32)))
+    if c.psac_basis is not None:
+        U = np.stack([np.stack([np.linalg.qr(r.standard_normal((D, 8)))[0] for _ in range(H)]) for _ in range(B)])
+        c.psac_basis.copy_(torch.from_numpy(np.ascontiguousarray(U, np.float32)))
+    kv.kv_quantize_append(c, dev_bf16(K), dev_bf16(V), 0)
+    q = synth.to_bf16_bits(r.standard_normal((B, Lq, H * G, D)).astype(np.float32))
+    _check(c, n, q, f"case {case}: D={D} mode={mode} B={B} H={H} G={G} n={n} Lq={Lq} C={C} R={R} fmt={fmt}")
