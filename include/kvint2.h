@@ -287,7 +287,12 @@ size_t attn_int2_chunk_workspace(const kvq_layout* L, int32_t q_len,
  * [B][q_len][q_heads][D] in out_dtype; lse_dev (nullable) f32
  * [B][q_heads][q_len].  Every query row sees every cached token (no mask);
  * the chunk's own keys/values are not included -- merge them with lse.
- * Same errors as attn_int2_decode. */
+ * Precision: fp16 MFMA operands with fp32 accumulation.  Window keys enter
+ * as fp16 hi + lo (exact to fp32); a centroid key enters as one fp16 value
+ * per element (centroid + residual summed in fp32, rounded once), so each
+ * logit term carries a relative error of up to 2^-11: within 2e-3 of the
+ * exact attention for keys near unit rms, growing with the key magnitudes
+ * beyond that.  Same errors as attn_int2_decode. */
 int attn_int2_chunk(const kvq_cache* cache, int32_t n_tokens,
                     const void* q_bf16_dev, int32_t q_len, int32_t q_heads,
                     float scale, void* out_dev, int32_t out_dtype,
