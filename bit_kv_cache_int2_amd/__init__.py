@@ -45,7 +45,7 @@ class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("batch", "kv_heads", "head_dim", "capacity",
                                                "key_mode", "value_mode", "n_centroids",
                                                "qsac_topk", "psac_rank", "qsac_score",
-                                               "psac_format")]
+                                               "psac_format", "centroid_key_split")]
 
 
 class CacheStruct(ctypes.Structure):
@@ -132,9 +132,11 @@ class KVCache:
     def __init__(self, batch: int, kv_heads: int, head_dim: int, capacity: int,
                  key_mode: int = KEY_WINDOW, value_mode: int = VAL_GROUP,
                  n_centroids: int = 0, qsac_topk: int = 1, psac_rank: int = 0,
-                 qsac_score: int = QSAC_EXACT, psac_format: int = PSAC_F16, device="cuda"):
+                 qsac_score: int = QSAC_EXACT, psac_format: int = PSAC_F16,
+                 centroid_key_split: bool = False, device="cuda"):
         self.layout = Layout(batch, kv_heads, head_dim, capacity, key_mode, value_mode,
-                             n_centroids, qsac_topk, psac_rank, qsac_score, psac_format)
+                             n_centroids, qsac_topk, psac_rank, qsac_score, psac_format,
+                             int(bool(centroid_key_split)))
         _check(lib().kvq_layout_check(ctypes.byref(self.layout)), "layout")
         B, H, D, T = batch, kv_heads, head_dim, capacity
         shapes = {

@@ -34,6 +34,8 @@ int check_layout(const kvq_layout* L) {
     return KVQ_EINVAL;
   if (L->psac_rank > 0 && L->psac_format != KVQ_PSAC_F16 && L->psac_format != KVQ_PSAC_INT8)
     return KVQ_EINVAL;
+  if (L->key_mode != KVQ_KEY_WINDOW && L->centroid_key_split != 0 && L->centroid_key_split != 1)
+    return KVQ_EINVAL;
   if ((int64_t)L->batch * L->kv_heads * L->capacity > ((int64_t)1 << 40)) return KVQ_EINVAL;
   return KVQ_OK;
 }

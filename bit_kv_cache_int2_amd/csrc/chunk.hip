@@ -87,7 +87,9 @@ template <int D, int KM, bool HAD, int R>
 __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
   constexpr int NKS = D / 32;        // QK k-steps
   constexpr int NDT = D / 16;        // PV output dim tiles
-  constexpr bool LO = (KM == 0);     // hi/lo split keys
+  // KM: 0 window keys, 1 centroid keys as one fp16 copy, 2 centroid keys
+  // split hi + lo like window keys
+  constexpr bool LO = (KM != 1);     // hi/lo split keys
   // Tile pitches of 2 (mod 4) 16-byte units let the sixteen rows one operand
   // read touches fall on distinct banks; odd key rows and every other pair
   // of value rows swap neighbouring 16-byte units, which spreads the tile
@@ -654,13 +656,19 @@ hipError_t launch_t(const ChunkArgs& a, int B, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int D, int KM>
+hipError_t launch_c(const ChunkArgs& a, bool had, int R, int B, hipStream_t st) {
+  if (R == 8)
+    return had ? launch_t<D, KM, true, 8>(a, B, st) : launch_t<D, KM, false, 8>(a, B, st);
+  return had ? launch_t<D, KM, true, 0>(a, B, st) : launch_t<D, KM, false, 0>(a, B, st);
+}
+
 template <int D>
-hipError_t launch_d(const ChunkArgs& a, int key_mode, bool had, int R, int B, hipStream_t st) {
+hipError_t launch_d(const ChunkArgs& a, int key_mode, bool split, bool had, int R, int B,
+                    hipStream_t st) {
   if (key_mode == KVQ_KEY_WINDOW)
     return had ? launch_t<D, 0, true, 0>(a, B, st) : launch_t<D, 0, false, 0>(a, B, st);
-  if (R == 8)
-    return had ? launch_t<D, 1, true, 8>(a, B, st) : launch_t<D, 1, false, 8>(a, B, st);
-  return had ? launch_t<D, 1, true, 0>(a, B, st) : launch_t<D, 1, false, 0>(a, B, st);
+  return split ? launch_c<D, 2>(a, had, R, B, st) : launch_c<D, 1>(a, had, R, B, st);
 }
 
 // Token splits.  One block of 8 waves is resident per CU; among split counts
@@ -738,8 +746,9 @@ hipError_t launch_chunk(const kvq_cache* c, int n_tokens, const void* q, int q_l
   chunk_splits(&L, q_len, q_heads, n_tokens, &a.S, &a.tiles_per_split);
   const int R = (L.key_mode == KVQ_KEY_WINDOW) ? 0 : L.psac_rank;
   const bool had = L.value_mode == KVQ_VAL_HADAMARD;
-  return (L.head_dim == 128) ? launch_d<128>(a, L.key_mode, had, R, L.batch, stream)
-                             : launch_d<64>(a, L.key_mode, had, R, L.batch, stream);
+  const bool split = L.centroid_key_split != 0;
+  return (L.head_dim == 128) ? launch_d<128>(a, L.key_mode, split, had, R, L.batch, stream)
+                             : launch_d<64>(a, L.key_mode, split, had, R, L.batch, stream);
 }
 
 }  // namespace kvq

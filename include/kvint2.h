@@ -130,6 +130,10 @@ typedef struct kvq_layout {
                           centroid modes only                          */
   int32_t qsac_score;  /* KVQ_QSAC_* (QSAC only; else ignored)         */
   int32_t psac_format; /* KVQ_PSAC_* (psac_rank > 0; else ignored)     */
+  int32_t centroid_key_split; /* chunk attention over centroid keys: 0 =
+                         one fp16 copy per key element (default), 1 = fp16
+                         hi + lo, exact to fp32 like window keys and about a
+                         third slower; 0 or 1 (centroid modes; else ignored) */
 } kvq_layout;
 
 /* Device buffers of one layer's packed cache.  Shapes are C order.
@@ -292,7 +296,11 @@ size_t attn_int2_chunk_workspace(const kvq_layout* L, int32_t q_len,
  * per element (centroid + residual summed in fp32, rounded once), so each
  * logit term carries a relative error of up to 2^-11: within 2e-3 of the
  * exact attention for keys near unit rms, growing with the key magnitudes
- * beyond that.  Same errors as attn_int2_decode. */
+ * beyond that, unless the layout sets centroid_key_split (hi + lo for
+ * centroid keys too).  Probabilities and dequantised values enter as one
+ * fp16 each: an error near 2^-11 max|v| where a few tokens carry the
+ * softmax (2e-3 is reached for values near 8).  Same errors as
+ * attn_int2_decode. */
 int attn_int2_chunk(const kvq_cache* cache, int32_t n_tokens,
                     const void* q_bf16_dev, int32_t q_len, int32_t q_heads,
                     float scale, void* out_dev, int32_t out_dtype,

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 def _layout(**kw):
     d = dict(batch=2, kv_heads=4, head_dim=128, capacity=1024, key_mode=kv.KEY_WINDOW,
              value_mode=kv.VAL_GROUP, n_centroids=0, qsac_topk=1, psac_rank=0, qsac_score=0,
-             psac_format=0)
+             psac_format=0, centroid_key_split=0)
     d.update(kw)
     return kv.Layout(*[d[f] for f, _ in kv.Layout._fields_])
 
@@ -47,6 +47,9 @@ def test_layout_validation():
     chk = lambda **kw: kv.lib().kvq_layout_check(ctypes.byref(_layout(**kw)))
     assert chk() == kv.KVQ_OK
     assert chk(capacity=1000) == kv.KVQ_EINVAL
+    assert chk(key_mode=kv.KEY_CENTROID, n_centroids=16, centroid_key_split=1) == kv.KVQ_OK
+    assert chk(key_mode=kv.KEY_CENTROID, n_centroids=16, centroid_key_split=2) == kv.KVQ_EINVAL
+    assert chk(centroid_key_split=2) == kv.KVQ_OK          # ignored for window keys
     assert chk(batch=0) == kv.KVQ_EINVAL
     assert chk(head_dim=96) == kv.KVQ_EUNSUPPORTED
     assert chk(key_mode=7) == kv.KVQ_EINVAL

@@ -64,7 +64,8 @@ def test_centroid_chunk(mode, R, had, fmt):
 
 
 @pytest.mark.parametrize("D,C", [(64, 1), (128, 256)])
-def test_centroid_chunk_large_keys_fp16_envelope(D, C):
+@pytest.mark.parametrize("split", [False, True])
+def test_centroid_chunk_large_keys_fp16_envelope(D, C, split):
     """Centroid keys far above unit rms (per-channel scales to 5, offsets of
     sd 1.5: rms about 2.4, peaks near 20).  The chunk kernel holds each
     dequantised centroid key as one fp16 value, the centroid plus residual
@@ -72,14 +73,17 @@ def test_centroid_chunk_large_keys_fp16_envelope(D, C):
     error of up to 2^-11 per term: against the exact attention that error
     reaches a few 1e-3 here.  Against the exact attention over the
     fp16-rounded keys (the same cache otherwise) it stays within the
-    tolerance, which pins the whole deviation on that one rounding."""
+    tolerance, which pins the whole deviation on that one rounding.  With
+    centroid_key_split the keys enter as hi + lo and the result is within
+    the tolerance of the exact attention itself."""
     rng = np.random.default_rng(31 + D)
     B, H, G, T, Lq = 1, 2, 2, 391, 144
     sc = np.exp(rng.uniform(np.log(0.2), np.log(5.0), (1, 1, H, D)))
     off = rng.normal(0, 1.5, (1, 1, H, D))
     K = synth.to_bf16_bits((rng.standard_normal((B, T, H, D)) * sc + off).astype(np.float32))
     V = synth.to_bf16_bits((rng.standard_normal((B, T, H, D)) * 1.5).astype(np.float32))
-    c = kv.KVCache(B, H, D, 448, key_mode=kv.KEY_CENTROID, n_centroids=C, value_mode=kv.VAL_GROUP)
+    c = kv.KVCache(B, H, D, 448, key_mode=kv.KEY_CENTROID, n_centroids=C, value_mode=kv.VAL_GROUP,
+                   centroid_key_split=split)
     Kf = synth.bf16_bits_to_f32(K)
     c.centroids.copy_(torch.from_numpy(np.ascontiguousarray(
         np.stack([[Kf[0, rng.integers(0, T, C), h] for h in range(H)]]), np.float32)))
@@ -101,6 +105,9 @@ def test_centroid_chunk_large_keys_fp16_envelope(D, C):
         ref = (p @ vh) / p.sum(axis=1, keepdims=True)
         err16 = max(err16, float(np.abs(got[0, :, hq] - ref).max()))
     err = float(np.abs(got - exact).max())
+    if split:
+        assert err <= TOL, f"D={D} C={C} split: {err:.3e} from exact attention"
+        return
     assert err16 <= TOL, f"D={D} C={C}: {err16:.3e} from attention over fp16 keys ({err:.3e} from exact)"
     assert err <= 8 * TOL, f"D={D} C={C}: {err:.3e} from exact attention"
 
