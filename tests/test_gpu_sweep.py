@@ -61,6 +61,20 @@ def test_random_long_configuration(case):
     _run(cfg, r, f"long case {case}", chunk_rows=slice(None, None, 5))
 
 
+@pytest.mark.parametrize("case", range(20))
+def test_random_streaming_appends(case):
+    """Tokens arrive a few at a time (1 to 17 per call, as in decoding or a
+    frame arriving in pieces): every call lands in a partly filled value
+    tile and window, through the merge with earlier codes and the key
+    tail; the cache must still equal the oracle's bit for bit."""
+    cfg, r = _draw(case, seed0=27000, t_range=(60, 400))
+    sizes = []
+    while sum(sizes) < cfg["T"]:
+        sizes.append(int(min(r.integers(1, 18), cfg["T"] - sum(sizes))))
+    cfg["chunks"] = sizes
+    _run(cfg, r, f"streaming case {case}")
+
+
 def _run(cfg, r, name, chunk_rows=None):
     D, B, H, T, G = cfg["D"], cfg["B"], cfg["H"], cfg["T"], cfg["G"]
     Hq = H * G
