@@ -108,10 +108,50 @@ def _ptr(t):
 
 
 def _need_cuda(t: torch.Tensor, name: str, dtype=None):
-    if not (t.is_cuda and t.is_contiguous()):
-        raise ValueError(f"{name} must be a contiguous device tensor")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def _need_shape(t: torch.Tensor, name: str, shape, dtypes) -> None:
+    """Shape and dtype of a tensor the C ABI cannot size-check (it reads or
+    writes exactly this many elements): checked before anything else."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be one of {dtypes}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _attention_io(cache: "KVCache", q: torch.Tensor, q_rank: int, qdtypes, out, out_dtype, lse,
+                  lse_shape):
+    """Validates q against the cache layout and the optional out / lse
+    against q, and allocates out when it is None."""
+    L = cache.layout
+    if q.dim() != q_rank:
+        raise ValueError(f"q must have {q_rank} dimensions, got {tuple(q.shape)}")
+    if q.dtype not in qdtypes:
+        raise ValueError(f"q must be one of {qdtypes}, got {q.dtype}")
+    if q.shape[0] != L.batch or q.shape[-1] != L.head_dim:
+        raise ValueError(f"q must be [batch={L.batch}, ..., head_dim={L.head_dim}], got {tuple(q.shape)}")
+    if out is None:
+        out = torch.empty(tuple(q.shape), dtype=out_dtype, device=q.device)
+    _need_shape(out, "out", q.shape, (torch.float32, torch.bfloat16))
+    if lse is not None:   # any contiguous f32 tensor of that many elements
+        want = 1
+        for x in lse_shape:
+            want *= int(x)
+        if lse.numel() != want:
+            raise ValueError(f"lse must have shape {tuple(lse_shape)} ({want} elements), "
+                             f"got {tuple(lse.shape)}")
+        _need_shape(lse, "lse", lse.shape, (torch.float32,))
+    _need_cuda(q, "q")
+    _need_cuda(out, "out")
+    if lse is not None:
+        _need_cuda(lse, "lse")
+    return out
 
 
 class KVCache:
@@ -251,18 +291,19 @@ def attn_int2_decode(cache: KVCache, n_tokens: int, q: torch.Tensor, scale: floa
                      out=None, out_dtype=torch.float32, lse=None, workspace=None,
                      stream=None) -> torch.Tensor:
     """q [B, Hq, D] (f32 or bf16) against the first n_tokens cached tokens."""
-    _need_cuda(q, "q")
+    out = _attention_io(cache, q, 3, (torch.float32, torch.bfloat16), out, out_dtype, lse,
+                        q.shape[:2])
     qd = {torch.float32: F32, torch.bfloat16: BF16}[q.dtype]
     B, Hq, D = q.shape
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
     od = {torch.float32: F32, torch.bfloat16: BF16}[out.dtype]
     if workspace is None:
         workspace = decode_workspace(cache, Hq, n_tokens, q.device)
+    _need_cuda(workspace, "workspace")
     cs = cache.struct()
     _check(lib().attn_int2_decode(ctypes.byref(cs), int(n_tokens), _ptr(q), qd, Hq, float(scale),
                                   _ptr(out), od, _ptr(lse), _ptr(workspace),
-                                  workspace.numel(), _stream(stream)), "attn_int2_decode")
+                                  workspace.numel() * workspace.element_size(), _stream(stream)),
+           "attn_int2_decode")
     return out
 
 
@@ -276,6 +317,9 @@ def attn_int2_top1(cache: KVCache, n_tokens: int, q: torch.Tensor, logits: bool 
                    stream=None):
     """Each query row's highest-logit cached token (q bf16 [B, Lq, Hq, D]):
     i32 [B, Hq, Lq], and with logits=True also the f32 logits."""
+    L = cache.layout
+    if q.dim() != 4 or q.shape[0] != L.batch or q.shape[3] != L.head_dim:
+        raise ValueError(f"q must be [batch={L.batch}, Lq, Hq, head_dim={L.head_dim}], got {tuple(q.shape)}")
     _need_cuda(q, "q", torch.bfloat16)
     B, Lq, Hq, D = q.shape
     idx = torch.empty((B, Hq, Lq), dtype=torch.int32, device=q.device)
@@ -290,15 +334,16 @@ def attn_int2_chunk(cache: KVCache, n_tokens: int, q: torch.Tensor, scale: float
                     out=None, out_dtype=torch.float32, lse=None, workspace=None,
                     stream=None) -> torch.Tensor:
     """q bf16 [B, Lq, Hq, D] against the first n_tokens cached tokens."""
-    _need_cuda(q, "q", torch.bfloat16)
+    out = _attention_io(cache, q, 4, (torch.bfloat16,), out, out_dtype, lse,
+                        (q.shape[0], q.shape[2], q.shape[1]))
     B, Lq, Hq, D = q.shape
-    if out is None:
-        out = torch.empty((B, Lq, Hq, D), dtype=out_dtype, device=q.device)
     od = {torch.float32: F32, torch.bfloat16: BF16}[out.dtype]
     if workspace is None:
         workspace = chunk_workspace(cache, Lq, Hq, n_tokens, q.device)
+    _need_cuda(workspace, "workspace")
     cs = cache.struct()
     _check(lib().attn_int2_chunk(ctypes.byref(cs), int(n_tokens), _ptr(q), Lq, Hq, float(scale),
-                                 _ptr(out), od, _ptr(lse), _ptr(workspace), workspace.numel(),
-                                 _stream(stream)), "attn_int2_chunk")
+                                 _ptr(out), od, _ptr(lse), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+           "attn_int2_chunk")
     return out

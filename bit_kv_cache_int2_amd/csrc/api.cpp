@@ -3,6 +3,7 @@
 // has passed, so error returns leave all outputs untouched.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "internal.h"
@@ -37,6 +38,10 @@ int check_layout(const kvq_layout* L) {
   if (L->key_mode != KVQ_KEY_WINDOW && L->centroid_key_split != 0 && L->centroid_key_split != 1)
     return KVQ_EINVAL;
   if ((int64_t)L->batch * L->kv_heads * L->capacity > ((int64_t)1 << 40)) return KVQ_EINVAL;
+  // grid dimensions (sequences and heads index grid y/z, at most 65535) and
+  // 32-bit token-row offsets within one (sequence, head)
+  if (L->batch > kvq::kMaxGridYZ || L->kv_heads > kvq::kMaxGridYZ) return KVQ_EUNSUPPORTED;
+  if (L->capacity > kvq::kMaxCapacity) return KVQ_EUNSUPPORTED;
   return KVQ_OK;
 }
 
@@ -95,12 +100,34 @@ int check_attention(const kvq_cache* c, int32_t n_tokens, const void* q, int32_t
   if (q_heads < 1 || q_heads % L.kv_heads != 0) return KVQ_EINVAL;
   const int G = q_heads / L.kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVQ_EUNSUPPORTED;
+  if (q_heads > kvq::kMaxGridYZ) return KVQ_EUNSUPPORTED;
   if (n_tokens < 1) return KVQ_EINVAL;
   if (n_tokens > L.capacity) return KVQ_ECAPACITY;
   return KVQ_OK;
 }
 
 }  // namespace
+
+namespace kvq {
+
+// Compute units of the current device, queried once per device.
+int device_cus() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cus[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < kMaxDev) {
+    const int v = cus[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    return 256;
+  if (dev >= 0 && dev < kMaxDev) cus[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+}  // namespace kvq
 
 extern "C" {
 
@@ -138,6 +165,9 @@ int kv_quantize_append(const kvq_cache* cache, const void* k_bf16, const void* v
   if ((int64_t)cur_len + n_new > cache->layout.capacity) return KVQ_ECAPACITY;
   if (n_new == 0) return KVQ_OK;
   if (!k_bf16 || !v_bf16 || !aligned16(k_bf16) || !aligned16(v_bf16)) return KVQ_EINVAL;
+  // one block row per 64-token window the append touches (grid y)
+  const int64_t end = (int64_t)cur_len + n_new;
+  if ((end - 1) / KVQ_WINDOW - cur_len / KVQ_WINDOW + 1 > kvq::kMaxGridYZ) return KVQ_EUNSUPPORTED;
   return hip_status(kvq::launch_quantize_append(cache, k_bf16, v_bf16, cur_len, n_new,
                                                 (hipStream_t)stream));
 }

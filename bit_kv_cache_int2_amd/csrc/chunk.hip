@@ -678,12 +678,7 @@ hipError_t launch_d(const ChunkArgs& a, int key_mode, bool split, bool had, int 
 void chunk_splits(const kvq_layout* L, int q_len, int q_heads, int n_tokens, int* S, int* per) {
   const int n_tiles = (n_tokens + 63) / 64;
   const int64_t blocks = (int64_t)((q_len + kBM - 1) / kBM) * q_heads * L->batch;
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      cus = v;
-  }
+  const int cus = device_cus();
   int best = 1, best_per = n_tiles > 0 ? n_tiles : 1;
   double best_cost = 1e300;
   for (int s = 1; s <= 64; ++s) {

@@ -902,12 +902,7 @@ int decode_splits(const kvq_layout* L, int q_heads, int n_tokens) {
   const int n_win = (n_tokens + kWindow - 1) / kWindow;
   if (n_win <= 0) return 1;
   const int64_t units = (int64_t)L->batch * L->kv_heads;
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      cus = v;
-  }
+  const int cus = device_cus();
   const int64_t slots = (int64_t)cus * kDecodeBlocksPerCU;
   const int s_min = (n_win + kDecodeMaxWindows - 1) / kDecodeMaxWindows;
   const int s_max = n_win < s_min * 16 ? n_win : s_min * 16;

@@ -9,6 +9,15 @@
 
 namespace kvq {
 
+// Largest grid y / z dimension (sequences, heads, windows of one append).
+constexpr int kMaxGridYZ = 65535;
+// Largest cache capacity per (sequence, head): token-row offsets inside one
+// (sequence, head) stay within 32 bits.
+constexpr int kMaxCapacity = 1 << 24;
+
+// Compute units of the current device (queried once per device).
+int device_cus();
+
 hipError_t launch_quantize_append(const kvq_cache* c, const void* k_bf16,
                                   const void* v_bf16, int cur_len, int n_new,
                                   hipStream_t stream);

@@ -121,7 +121,8 @@ typedef struct kvq_layout {
   int32_t batch;       /* sequences B                                  */
   int32_t kv_heads;    /* KV heads H                                   */
   int32_t head_dim;    /* D: 64 or 128                                 */
-  int32_t capacity;    /* Tcap tokens per sequence, a multiple of 64   */
+  int32_t capacity;    /* Tcap tokens per sequence, a multiple of 64,
+                          at most 2^24                                 */
   int32_t key_mode;    /* KVQ_KEY_*                                    */
   int32_t value_mode;  /* KVQ_VAL_*                                    */
   int32_t n_centroids; /* C, 1..256 (centroid modes; else ignored)     */
@@ -197,7 +198,10 @@ enum {
  * does not use it or L is invalid.  Host only, no device access. */
 size_t kvq_buffer_bytes(const kvq_layout* L, int32_t which);
 
-/* Checks a layout; returns KVQ_OK, KVQ_EINVAL or KVQ_EUNSUPPORTED. */
+/* Checks a layout; returns KVQ_OK, KVQ_EINVAL or KVQ_EUNSUPPORTED
+ * (head_dim, centroid count or PSAC rank not built; batch or kv_heads above
+ * 65535 or capacity above 2^24, the limits of the launch grids and of the
+ * 32-bit row offsets inside one (sequence, head)). */
 int kvq_layout_check(const kvq_layout* L);
 
 /* ------------------------------------------------------------ append */
@@ -210,8 +214,14 @@ int kvq_layout_check(const kvq_layout* L);
  * channel from the tail and the new tokens; the tokens of the window left
  * unfinished are written to the tail.  The cache bytes depend on the token
  * sequence only, not on how it was split into appends.
+ * The library keeps no length: the caller passes it.  With window keys,
+ * cur_len must be the number of tokens appended so far, or a multiple of
+ * 64 below it (a rewind to a window boundary, after which the later tokens
+ * are overwritten): the append completes the unfinished window from the
+ * tail, which holds the tokens of the last window only.
  * Errors: KVQ_EINVAL (null buffer a mode needs, cur_len < 0, n_new < 0),
- * KVQ_ECAPACITY (cur_len + n_new > capacity). n_new == 0 is a no-op. */
+ * KVQ_ECAPACITY (cur_len + n_new > capacity), KVQ_EUNSUPPORTED (the append
+ * touches more than 65535 windows). n_new == 0 is a no-op. */
 int kv_quantize_append(const kvq_cache* cache, const void* k_bf16_dev,
                        const void* v_bf16_dev, int32_t cur_len, int32_t n_new,
                        void* stream);
@@ -271,9 +281,14 @@ size_t attn_int2_decode_workspace(const kvq_layout* L, int32_t q_heads,
  * to the input basis for KVQ_VAL_HADAMARD; lse_dev (nullable) f32
  * [B][q_heads] = log sum_t exp(scale * logit_t).  Logits include the PSAC
  * term (U^T q) . a_t when psac_rank > 0.  No mask.  ws_dev: scratch of
- * attn_int2_decode_workspace() bytes.  Errors: KVQ_EINVAL (nulls, q_heads
- * not a multiple of H, n_tokens < 1), KVQ_EUNSUPPORTED (q_heads / H not in
- * {1,2,4,8}), KVQ_ECAPACITY (n_tokens > capacity), KVQ_EWORKSPACE. */
+ * attn_int2_decode_workspace() bytes.
+ * With window keys the tokens of an unfinished window are read from the
+ * tail, which holds the last window of the appended sequence only: n_tokens
+ * must be the number of tokens appended so far, or a multiple of 64 not
+ * above it (a prefix of whole windows).
+ * Errors: KVQ_EINVAL (nulls, q_heads not a multiple of H, n_tokens < 1),
+ * KVQ_EUNSUPPORTED (q_heads / H not in {1,2,4,8}, q_heads above 65535),
+ * KVQ_ECAPACITY (n_tokens > capacity), KVQ_EWORKSPACE. */
 int attn_int2_decode(const kvq_cache* cache, int32_t n_tokens,
                      const void* q_dev, int32_t q_dtype, int32_t q_heads,
                      float scale, void* out_dev, int32_t out_dtype,
@@ -299,8 +314,8 @@ size_t attn_int2_chunk_workspace(const kvq_layout* L, int32_t q_len,
  * beyond that, unless the layout sets centroid_key_split (hi + lo for
  * centroid keys too).  Probabilities and dequantised values enter as one
  * fp16 each: an error near 2^-11 max|v| where a few tokens carry the
- * softmax (2e-3 is reached for values near 8).  Same errors as
- * attn_int2_decode. */
+ * softmax (2e-3 is reached for values near 8).  Same window-key contract
+ * on n_tokens and same errors as attn_int2_decode. */
 int attn_int2_chunk(const kvq_cache* cache, int32_t n_tokens,
                     const void* q_bf16_dev, int32_t q_len, int32_t q_heads,
                     float scale, void* out_dev, int32_t out_dtype,

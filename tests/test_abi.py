@@ -66,6 +66,12 @@ def test_layout_validation():
     assert chk(**q, psac_rank=8, psac_format=kv.PSAC_INT8) == kv.KVQ_OK
     assert chk(**q, psac_rank=8, psac_format=3) == kv.KVQ_EINVAL
     assert chk(key_mode=kv.KEY_CENTROID, n_centroids=16, qsac_score=5) == kv.KVQ_OK   # ignored
+    # launch-grid and 32-bit row-offset limits
+    assert chk(batch=1, kv_heads=1, capacity=1 << 24) == kv.KVQ_OK
+    assert chk(batch=1, kv_heads=1, capacity=(1 << 24) + 64) == kv.KVQ_EUNSUPPORTED
+    assert chk(batch=65535, kv_heads=1, capacity=64) == kv.KVQ_OK
+    assert chk(batch=65536, kv_heads=1, capacity=64) == kv.KVQ_EUNSUPPORTED
+    assert chk(batch=1, kv_heads=65536, capacity=64) == kv.KVQ_EUNSUPPORTED
 
 
 def test_buffer_sizes():
@@ -109,6 +115,10 @@ def test_append_validation_without_launch():
     mis = _cache()
     mis.k_codes = ctypes.c_void_p((1 << 20) + 4)
     assert L.kv_quantize_append(ctypes.byref(mis), p, p, 0, 1, None) == kv.KVQ_EINVAL
+    # an append touching more than 65535 windows (grid y) is refused
+    big = _cache(batch=1, kv_heads=1, capacity=1 << 24)
+    assert L.kv_quantize_append(ctypes.byref(big), p, p, 0, 65536 * 64, None) == kv.KVQ_EUNSUPPORTED
+    assert L.kv_quantize_append(ctypes.byref(big), p, p, 32, 65535 * 64, None) == kv.KVQ_EUNSUPPORTED
 
 
 def test_attention_validation_without_launch():
@@ -137,6 +147,51 @@ def test_attention_validation_without_launch():
     assert top1(n=0) == kv.KVQ_EINVAL
     assert top1(n=2000) == kv.KVQ_ECAPACITY
     assert top1(idx=None) == kv.KVQ_EINVAL
+    # more than 65535 query heads (grid y) is refused before any launch
+    wide = _cache(batch=1, kv_heads=16384, capacity=64)
+    assert L.attn_int2_decode(ctypes.byref(wide), 64, p, kv.F32, 16384 * 8, 0.1, p, kv.F32, None,
+                              p, 1 << 40, None) == kv.KVQ_EUNSUPPORTED
+    assert L.attn_int2_chunk(ctypes.byref(wide), 64, p, 4, 16384 * 8, 0.1, p, kv.F32, None,
+                             p, 1 << 40, None) == kv.KVQ_EUNSUPPORTED
+
+
+def test_python_wrappers_check_shapes_before_any_call():
+    """The bindings size-check what the C ABI cannot (q, out, lse against
+    the layout) and raise ValueError before reaching the library; CPU
+    tensors suffice because the checks come first."""
+    import torch
+    c = kv.KVCache(2, 4, 128, 1024, device="cpu")
+    q = torch.zeros((2, 8, 128))
+    with pytest.raises(ValueError, match="batch"):
+        kv.attn_int2_decode(c, 100, torch.zeros((3, 8, 128)), 0.1)
+    with pytest.raises(ValueError, match="head_dim"):
+        kv.attn_int2_decode(c, 100, torch.zeros((2, 8, 64)), 0.1)
+    with pytest.raises(ValueError, match="dimensions"):
+        kv.attn_int2_decode(c, 100, torch.zeros((2, 1, 8, 128)), 0.1)
+    with pytest.raises(ValueError, match="out must have shape"):
+        kv.attn_int2_decode(c, 100, q, 0.1, out=torch.zeros((2, 8, 64)))
+    with pytest.raises(ValueError, match="out must be one of"):
+        kv.attn_int2_decode(c, 100, q, 0.1, out=torch.zeros((2, 8, 128), dtype=torch.float16))
+    with pytest.raises(ValueError, match="out must be contiguous"):
+        kv.attn_int2_decode(c, 100, q, 0.1, out=torch.zeros((2, 128, 8)).transpose(1, 2))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        kv.attn_int2_decode(c, 100, q, 0.1, lse=torch.zeros((2, 4)))
+    with pytest.raises(ValueError, match="lse must be one of"):
+        kv.attn_int2_decode(c, 100, q, 0.1, lse=torch.zeros((2, 8), dtype=torch.float64))
+    qc = torch.zeros((2, 5, 8, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="q must be one of"):
+        kv.attn_int2_chunk(c, 100, qc.float(), 0.1)
+    with pytest.raises(ValueError, match="batch"):
+        kv.attn_int2_chunk(c, 100, torch.zeros((1, 5, 8, 128), dtype=torch.bfloat16), 0.1)
+    with pytest.raises(ValueError, match="lse must have shape"):
+        kv.attn_int2_chunk(c, 100, qc, 0.1, lse=torch.zeros((2, 5, 7)))
+    with pytest.raises(ValueError, match="out must have shape"):
+        kv.attn_int2_chunk(c, 100, qc, 0.1, out=torch.zeros((2, 5, 8, 64)))
+    with pytest.raises(ValueError, match="head_dim"):
+        kv.attn_int2_top1(c, 100, torch.zeros((2, 5, 8, 64), dtype=torch.bfloat16))
+    # shapes right, but host tensors: refused by the device check
+    with pytest.raises(ValueError, match="device"):
+        kv.attn_int2_decode(c, 100, q, 0.1)
 
 
 def test_assign_validation_without_launch():
@@ -159,7 +214,6 @@ def test_kmeans_validation_without_launch():
 
     def call(n=1000, B=2, H=3, D=128, ks=384, hs=128, bs=384000, C=16, it=2, w=p, wsb=ws):
         return L.kv_kmeans(p, B, n, H, D, ks, hs, bs, p, C, it, p, w, wsb, None)
-    assert call() == kv.KVQ_OK or True   # (a launch; not made here)
     assert call(n=-1) == kv.KVQ_EINVAL
     assert call(it=-1) == kv.KVQ_EINVAL
     assert call(B=-1) == kv.KVQ_EINVAL

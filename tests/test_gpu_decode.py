@@ -147,3 +147,37 @@ def test_llm_decode_full_size_sampled():
         worst = max(worst, err)
         assert err <= TOL, f"b={b} h={h} err {err}"
     print(f"full-size decode worst |delta| {worst:.3e}")
+
+
+def test_window_prefix_and_rewind():
+    """Window keys under the header's length contract: after appends past a
+    window boundary, attention over a prefix of whole windows reads only
+    their codes (decode and chunk match the oracle's cache of that prefix);
+    an append that rewinds to a window boundary overwrites the later tokens
+    and leaves the cache equal to a one-shot build of the new sequence."""
+    H, G, T, P = 2, 4, 300, 256
+    d = synth.llm_decode(B=1, Hkv=H, Hq=H * G, D=128, T=T)
+    c = kv.KVCache(1, H, 128, 320)
+    kv.kv_quantize_append(c, dev_bf16(d["K"][:, :100]), dev_bf16(d["V"][:, :100]), 0)
+    kv.kv_quantize_append(c, dev_bf16(d["K"][:, 100:]), dev_bf16(d["V"][:, 100:]), 100)
+    o = oracle_like(c)
+    o.append(np.ascontiguousarray(d["K"][:, :P]), np.ascontiguousarray(d["V"][:, :P]), 0)
+    qd = dev_bf16(d["q"])
+    q64 = synth.bf16_bits_to_f32(d["q"]).astype(np.float64)
+    scale = 1 / math.sqrt(128)
+    _decode_check(c, o, P, qd, q64, scale, "prefix of 4 windows")
+    rng = np.random.default_rng(5)
+    qc = synth.to_bf16_bits(rng.standard_normal((1, 40, H * G, 128)).astype(np.float32))
+    outc = kv.attn_int2_chunk(c, P, dev_bf16(qc), scale)
+    torch.cuda.synchronize()
+    refc, _ = o.attention(synth.bf16_bits_to_f32(qc).astype(np.float64), P, scale)
+    err = np.abs(outc.cpu().numpy().astype(np.float64) - refc).max()
+    assert err <= TOL, f"chunk over the prefix: {err:.3e}"
+    # rewind to the window boundary and append different tokens
+    K2, V2 = d["K"].copy(), d["V"].copy()
+    K2[:, P:] = synth.to_bf16_bits(rng.standard_normal(K2[:, P:].shape).astype(np.float32) * 3)
+    V2[:, P:] = synth.to_bf16_bits(rng.standard_normal(V2[:, P:].shape).astype(np.float32))
+    kv.kv_quantize_append(c, dev_bf16(K2[:, P:]), dev_bf16(V2[:, P:]), P)
+    o2 = oracle_like(c)
+    o2.append(K2, V2, 0)
+    _decode_check(c, o2, T, qd, q64, scale, "after the rewind")

@@ -3,6 +3,7 @@ per-token value groups (plain and rotated), centroid + residual keys, QSAC
 and PSAC.  Checks are against error bounds, brute force with independent
 fp64 numpy arithmetic, and append-order invariance."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -232,3 +233,45 @@ def test_psac_reduces_logit_error():
     base = np.abs(q @ (K.astype(np.float64) - kh).T).mean()
     comp = np.abs(q @ (K.astype(np.float64) - kt).T).mean()
     assert comp < 0.8 * base
+
+
+def _read_value_tile_fixture():
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "value_tile_bytes.txt")
+    values, bytes_, params = [], [], None
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        f = [x.strip() for x in line.split("|")]
+        if f[0] == "value":
+            values.append((f[1], int(f[2]), float(f[3])))
+        elif f[0] == "byte":
+            lo, _, hi = f[1].partition("..")
+            bytes_.append((int(lo), int(hi or lo), int(f[2], 16)))
+        elif f[0] == "param":
+            params = int(f[2], 16)
+    return values, bytes_, params
+
+
+def test_value_tile_byte_order_golden():
+    """The channel-major value tile against hand-derived bytes
+    (tests/golden/value_tile_bytes.txt): writer and reader cannot share a
+    transposition that this fixture would not see."""
+    values, bytes_, params = _read_value_tile_fixture()
+    D, T = 64, 64
+    V = np.zeros((1, T, 1, D), np.float32)
+    for tok, ch, val in values:
+        if tok == "all":
+            V[0, :, 0, ch] = val
+        else:
+            V[0, int(tok), 0, ch] = val
+    K = np.zeros((1, T, 1, D), np.float32)
+    c = oracle.Cache(1, 1, D, T, oracle.KEY_WINDOW, oracle.VAL_GROUP)
+    c.append(synth.to_bf16_bits(K), synth.to_bf16_bits(V), 0)
+    want = np.zeros(T * D // 4, np.uint8)
+    for lo, hi, b in bytes_:
+        want[lo:hi + 1] = b
+    got = np.ascontiguousarray(c.v_codes).reshape(-1)
+    assert got.size == want.size
+    assert np.array_equal(got, want), np.nonzero(got != want)[0][:10]
+    assert np.all(np.ascontiguousarray(c.v_params).reshape(-1) == params)
