@@ -28,7 +28,7 @@ _lib = None
 GROUP = 32
 WINDOW = 64
 KEY_WINDOW, KEY_CENTROID, KEY_CENTROID_QSAC = 0, 1, 2
-VAL_GROUP, VAL_HADAMARD = 0, 1
+VAL_GROUP, VAL_HADAMARD, VAL_HADAMARD_MODAL = 0, 1, 2
 
 
 def lib():
@@ -54,17 +54,19 @@ def lib():
     L.orc_wht_f32.restype = None
     L.orc_wht_f64.argtypes = [vp, i32]
     L.orc_wht_f64.restype = None
+    L.orc_rotate_modal_f32.argtypes = [vp, i32, vp]
+    L.orc_rotate_modal_f32.restype = None
     L.orc_assign_plain.argtypes = [vp, vp, i32, i32]
     L.orc_assign_plain.restype = i32
     L.orc_assign_qsac.argtypes = [vp, vp, i32, i32, vp, i32, i32]
     L.orc_assign_qsac.restype = i32
-    L.orc_quantize_append.argtypes = [i32] * 11 + [vp] * 12 + [vp, vp, i32, i32]
+    L.orc_quantize_append.argtypes = [i32] * 12 + [vp] * 14 + [vp, vp, i32, i32]
     L.orc_quantize_append.restype = i32
     L.orc_dequant_keys.argtypes = [i32] * 6 + [vp] * 5 + [i32, i32, i32, vp]
     L.orc_dequant_keys.restype = None
     L.orc_dequant_values.argtypes = [i32, i32, i32, vp, vp, i32, i32, i32, vp]
     L.orc_dequant_values.restype = None
-    L.orc_attention.argtypes = ([i32] * 9 + [vp] * 11 + [i32, vp, i32, i32, dbl, vp, vp])
+    L.orc_attention.argtypes = ([i32] * 10 + [vp] * 13 + [i32, vp, i32, i32, dbl, vp, vp])
     L.orc_attention.restype = i32
     L.orc_top1.argtypes = [i32] * 8 + [vp] * 9 + [i32, vp, i32, i32, vp, vp]
     L.orc_top1.restype = i32
@@ -138,6 +140,16 @@ def wht_f32(x: np.ndarray) -> np.ndarray:
 def wht_f64(x: np.ndarray) -> np.ndarray:
     y = np.array(x, np.float64, copy=True, order="C")
     lib().orc_wht_f64(_p(y), y.size)
+    return y
+
+
+def rotate_modal_f32(x: np.ndarray, signs_row: np.ndarray) -> np.ndarray:
+    """One modality's value rotation of an f32 row: the WHT, then the
+    channels whose sign bit is set negated (signs_row u32 [D/32])."""
+    y = np.array(x, np.float32, copy=True, order="C")
+    sr = np.ascontiguousarray(signs_row, np.uint32)
+    assert sr.size == y.size // 32
+    lib().orc_rotate_modal_f32(_p(y), y.size, _p(sr))
     return y
 
 
@@ -215,6 +227,7 @@ class Cache:
     R: int = 0
     qsac_score: int = 0        # QSAC_EXACT / QSAC_RANGE
     psac_fmt: int = 0          # PSAC_F16 / PSAC_INT8
+    M: int = 1                 # modalities (VAL_HADAMARD_MODAL)
     k_codes: np.ndarray = field(default=None, repr=False)
     k_params: np.ndarray = field(default=None, repr=False)
     k_tail: np.ndarray = field(default=None, repr=False)
@@ -227,6 +240,8 @@ class Cache:
     k_psac_sc: np.ndarray = field(default=None, repr=False)
     v_codes: np.ndarray = field(default=None, repr=False)
     v_params: np.ndarray = field(default=None, repr=False)
+    v_signs: np.ndarray = field(default=None, repr=False)     # u32 [H][M][D/32] sign bits
+    v_modal: np.ndarray = field(default=None, repr=False)     # u8 [B][Tcap] modality per token
 
     def __post_init__(self):
         B, H, D, T = self.B, self.H, self.D, self.Tcap
@@ -257,6 +272,10 @@ class Cache:
             self.k_psac8 = z((B, H, T, max(self.R, 1)), np.int8)
         if self.k_psac_sc is None:
             self.k_psac_sc = z((B, H, T), np.uint16)
+        if self.v_signs is None:
+            self.v_signs = z((H, max(self.M, 1), D // 32), np.uint32)
+        if self.v_modal is None:
+            self.v_modal = z((B, T), np.uint8)
 
     def bufs(self):
         return [self.k_codes, self.k_params, self.k_tail, self.k_idx, self.centroids,
@@ -272,8 +291,8 @@ class Cache:
         assert (B, H, D) == (self.B, self.H, self.D) and v.shape == k.shape
         rc = lib().orc_quantize_append(
             self.B, self.H, self.D, self.Tcap, self.key_mode, self.value_mode,
-            self.C, self.topk, self.R, self.qsac_score, self.psac_fmt,
-            *[_p(b) for b in self.bufs()],
+            self.C, self.topk, self.R, self.qsac_score, self.psac_fmt, self.M,
+            _p(self.v_signs), _p(self.v_modal), *[_p(b) for b in self.bufs()],
             _p(k), _p(v), int(cur_len), int(n_new))
         if rc != 0:
             raise ValueError(f"orc_quantize_append failed: {rc}")
@@ -299,7 +318,8 @@ class Cache:
         lse = np.empty((B, Hq, Lq), np.float64)
         rc = lib().orc_attention(
             self.B, self.H, self.D, self.Tcap, self.key_mode, self.value_mode,
-            max(self.C, 1), self.R, self.psac_fmt, _p(self.k_codes), _p(self.k_params),
+            max(self.C, 1), self.R, self.psac_fmt, self.M, _p(self.v_signs), _p(self.v_modal),
+            _p(self.k_codes), _p(self.k_params),
             _p(self.k_tail), _p(self.k_idx), _p(self.centroids), _p(self.psac_basis),
             _p(self.k_psac), _p(self.k_psac8), _p(self.k_psac_sc), _p(self.v_codes),
             _p(self.v_params), int(n), _p(q), Lq, Hq, float(scale), _p(out), _p(lse))
@@ -327,5 +347,7 @@ class Cache:
         """A one-sequence, one-head copy (for sampled checks at full size)."""
         sl = lambda a: np.ascontiguousarray(a[b:b + 1, h:h + 1])
         return Cache(1, 1, self.D, self.Tcap, self.key_mode, self.value_mode, self.C,
-                     self.topk, self.R, self.qsac_score, self.psac_fmt,
-                     *[sl(a) for a in self.bufs()])
+                     self.topk, self.R, self.qsac_score, self.psac_fmt, self.M,
+                     *[sl(a) for a in self.bufs()],
+                     v_signs=np.ascontiguousarray(self.v_signs[h:h + 1]),
+                     v_modal=np.ascontiguousarray(self.v_modal[b:b + 1]))

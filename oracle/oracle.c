@@ -12,7 +12,8 @@
  *  [QWM]  "QuantWM: Training-Free 2-bit KV Cache Quantization for Stable
  *         Video World Models", section "QuantWM Framework": 1. QSAC, 2. PSAC.
  *  [OKV]  "OmniKVQuant: KV Cache Quantization for Omni-LLMs", English
- *         abstract: per-window key ranges, rotated values, fused decode.
+ *         abstract: per-window key ranges, rotated values (separately per
+ *         modality), fused decode.
  *  [WUSH] "WUSH-KV Applies Data-Adaptive Transforms to KV Cache
  *         Quantization": affine (min/max) low-bit quantizer.
  * The pages give no formulas; where they are silent the reading used is
@@ -33,7 +34,7 @@
 #define WINDOW 64 /* tokens per key-range window          */
 
 enum { KEY_WINDOW = 0, KEY_CENTROID = 1, KEY_CENTROID_QSAC = 2 };
-enum { VAL_GROUP = 0, VAL_HADAMARD = 1 };
+enum { VAL_GROUP = 0, VAL_HADAMARD = 1, VAL_HADAMARD_MODAL = 2 };
 
 /* OpenMP threads the oracle's parallel loops may use. */
 int orc_num_threads(void) { return omp_get_max_threads(); }
@@ -173,6 +174,25 @@ void orc_wht_f64(double* x, int D) {
       }
   double c = 1.0 / sqrt((double)D);
   for (int i = 0; i < D; ++i) x[i] *= c;
+}
+
+/* Per-modality rotation ([OKV] rotates values separately per modality;
+ * the page does not say how the rotations differ).  Reading: modality m
+ * of a head has its own sign vector sigma_m in {+1,-1}^D and the rotation
+ * R_m = diag(sigma_m) H, H the orthonormal Walsh-Hadamard transform above:
+ * the rotated row is orc_wht_f32(x) with channel c negated where
+ * sigma_m[c] = -1 (a negation is exact).  R_m is orthogonal and
+ * R_m^T = H diag(sigma_m), so attention rotates back with one H after
+ * summing p_t sigma_m(t) . vhat_t over the tokens of every modality.
+ * Signs: bit c % 32 of word c / 32 of the modality's row set means -1. */
+static int modal_sign(const uint32_t* signs_row, int c) {
+  return (signs_row[c / 32] >> (c % 32)) & 1u;
+}
+
+void orc_rotate_modal_f32(float* x, int D, const uint32_t* signs_row) {
+  orc_wht_f32(x, D);
+  for (int c = 0; c < D; ++c)
+    if (modal_sign(signs_row, c)) x[c] = -x[c];
 }
 
 /* ------------------------------------------------------------------ */
@@ -330,6 +350,9 @@ int orc_assign_qsac(const float* k, const float* cent, int C, int D,
 /* ------------------------------------------------------------------ */
 typedef struct {
   int B, H, D, Tcap, key_mode, value_mode, C, topk, R, qsac_score, psac_fmt;
+  int M;                    /* modalities (VAL_HADAMARD_MODAL)             */
+  const uint32_t* v_signs;  /* u32 [H][M][D/32] sign bits                  */
+  const uint8_t* v_modal;   /* u8 [B][Tcap] modality of each token         */
 } layout_t;
 
 static size_t bh(const layout_t* L, int b, int h) {
@@ -342,13 +365,17 @@ static uint8_t* value_code_byte(uint8_t* v_codes, size_t s, int Tcap, int D, int
          (p % WINDOW) / 4;
 }
 
-static void quantize_value_row(const layout_t* L, const uint16_t* v,
+static void quantize_value_row(const layout_t* L, const uint16_t* v, int b, int h,
                                uint8_t* v_codes, size_t s, int p, uint32_t* prm) {
   int D = L->D;
   float x[256];
   uint8_t codes[256];
   for (int d = 0; d < D; ++d) x[d] = orc_bf16_to_f32(v[d]);
   if (L->value_mode == VAL_HADAMARD) orc_wht_f32(x, D);
+  if (L->value_mode == VAL_HADAMARD_MODAL) {
+    const int m = L->v_modal[(size_t)b * L->Tcap + p];
+    orc_rotate_modal_f32(x, D, L->v_signs + ((size_t)h * L->M + m) * (D / 32));
+  }
   for (int g = 0; g < D / GROUP; ++g) {
     uint16_t sh, zh;
     orc_q2(x + g * GROUP, GROUP, 1, codes + g * GROUP, &sh, &zh);
@@ -419,15 +446,23 @@ static void quantize_centroid_key(const layout_t* L, const uint16_t* kin,
  * into appends. */
 int orc_quantize_append(int B, int H, int D, int Tcap, int key_mode,
                         int value_mode, int C, int topk, int R, int qsac_score,
-                        int psac_fmt, uint8_t* k_codes, uint32_t* k_params,
+                        int psac_fmt, int M, const uint32_t* v_signs,
+                        const uint8_t* v_modal, uint8_t* k_codes, uint32_t* k_params,
                         uint16_t* k_tail, uint8_t* k_idx, const float* centroids,
                         const float* sens_w, const float* psac_basis,
                         uint16_t* k_psac, int8_t* k_psac8, uint16_t* k_psac_sc,
                         uint8_t* v_codes, uint32_t* v_params,
                         const uint16_t* k_in, const uint16_t* v_in, int cur_len,
                         int n_new) {
-  layout_t L = {B, H, D, Tcap, key_mode, value_mode, C, topk, R, qsac_score, psac_fmt};
+  layout_t L = {B, H, D, Tcap, key_mode, value_mode, C, topk, R, qsac_score, psac_fmt,
+                M, v_signs, v_modal};
   if (cur_len < 0 || n_new < 0 || cur_len + n_new > Tcap) return -3;
+  if (value_mode == VAL_HADAMARD_MODAL) {
+    if (M < 1 || !v_signs || !v_modal) return -1;
+    for (int b = 0; b < B; ++b)
+      for (int i = 0; i < n_new; ++i)
+        if (v_modal[(size_t)b * Tcap + cur_len + i] >= M) return -1;
+  }
   const int rb = D / 4, ng = D / GROUP;
 #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int b = 0; b < B; ++b)
@@ -436,7 +471,7 @@ int orc_quantize_append(int B, int H, int D, int Tcap, int key_mode,
       for (int i = 0; i < n_new; ++i) {
         int p = cur_len + i;
         const uint16_t* v = v_in + (((size_t)b * n_new + i) * H + h) * D;
-        quantize_value_row(&L, v, v_codes, s, p, v_params + (s * Tcap + p) * ng);
+        quantize_value_row(&L, v, b, h, v_codes, s, p, v_params + (s * Tcap + p) * ng);
       }
       if (key_mode == KEY_WINDOW) {
         uint16_t* tail = k_tail + s * WINDOW * D;
@@ -548,7 +583,8 @@ void orc_dequant_values(int H, int D, int Tcap, const uint8_t* v_codes,
 /* q f64 [B][Lq][Hq][D]; out f64 [B][Lq][Hq][D]; lse f64 [B][Hq][Lq].     */
 /* ------------------------------------------------------------------ */
 int orc_attention(int B, int H, int D, int Tcap, int key_mode, int value_mode,
-                  int C, int R, int psac_fmt, const uint8_t* k_codes,
+                  int C, int R, int psac_fmt, int M, const uint32_t* v_signs,
+                  const uint8_t* v_modal, const uint8_t* k_codes,
                   const uint32_t* k_params, const uint16_t* k_tail,
                   const uint8_t* k_idx, const float* centroids,
                   const float* psac_basis, const uint16_t* k_psac,
@@ -557,6 +593,7 @@ int orc_attention(int B, int H, int D, int Tcap, int key_mode, int value_mode,
                   const uint32_t* v_params, int n, const double* q, int Lq,
                   int Hq, double scale, double* out, double* lse) {
   if (Hq % H != 0 || n < 1) return -1;
+  if (value_mode == VAL_HADAMARD_MODAL && (M < 1 || !v_signs || !v_modal)) return -1;
   const int grp = Hq / H;
   for (int b = 0; b < B; ++b)
     for (int h = 0; h < H; ++h) {
@@ -570,6 +607,20 @@ int orc_attention(int B, int H, int D, int Tcap, int key_mode, int value_mode,
       orc_dequant_keys(B, H, D, Tcap, key_mode, C, k_codes, k_params, k_tail,
                        k_idx, centroids, b, h, n, kh);
       orc_dequant_values(H, D, Tcap, v_codes, v_params, b, h, n, vh);
+      /* per-modality rotation: R_m^T = H diag(sigma_m), so each rotated
+       * value takes its modality's signs before the one final H */
+      if (value_mode == VAL_HADAMARD_MODAL)
+        for (int t = 0; t < n; ++t) {
+          const int m = v_modal[(size_t)b * Tcap + t];
+          if (m >= M) {
+            free(kh);
+            free(vh);
+            return -1;
+          }
+          const uint32_t* row = v_signs + ((size_t)h * M + m) * (D / 32);
+          for (int d = 0; d < D; ++d)
+            if (modal_sign(row, d)) vh[(size_t)t * D + d] = -vh[(size_t)t * D + d];
+        }
       size_t s = (size_t)b * H + h;
 #pragma omp parallel for collapse(2) schedule(dynamic)
       for (int g = 0; g < grp; ++g)
@@ -604,7 +655,7 @@ int orc_attention(int B, int H, int D, int Tcap, int key_mode, int value_mode,
             double p = lg[t] / sum;
             for (int d = 0; d < D; ++d) o[d] += p * vh[(size_t)t * D + d];
           }
-          if (value_mode == VAL_HADAMARD) orc_wht_f64(o, D);
+          if (value_mode == VAL_HADAMARD || value_mode == VAL_HADAMARD_MODAL) orc_wht_f64(o, D);
           double* oo = out + (((size_t)b * Lq + i) * Hq + hq) * D;
           for (int d = 0; d < D; ++d) oo[d] = o[d];
           lse[((size_t)b * Hq + hq) * Lq + i] = mx + log(sum);
