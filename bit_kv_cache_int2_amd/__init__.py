@@ -23,6 +23,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvint2.so")
 
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ECAPACITY, KVQ_EWORKSPACE, KVQ_EHIP = 0, -1, -2, -3, -4, -5
+KVQ_ESCRATCH = -6
+NOALLOC_SCRATCH_BYTES = 16 << 20   # KVQ_NOALLOC_SCRATCH_BYTES
 KEY_WINDOW, KEY_CENTROID, KEY_CENTROID_QSAC = 0, 1, 2
 VAL_GROUP, VAL_HADAMARD = 0, 1
 F32, BF16 = 0, 1
@@ -83,6 +85,8 @@ def lib():
     L.attn_int2_decode_workspace.restype = sz
     L.attn_int2_decode.argtypes = [pC, i32, vp, i32, i32, ctypes.c_float, vp, i32, vp, vp, sz, vp]
     L.attn_int2_decode.restype = ctypes.c_int
+    L.attn_int2_decode_noalloc.argtypes = [pC, i32, vp, i32, i32, ctypes.c_float, vp, i32, vp, vp]
+    L.attn_int2_decode_noalloc.restype = ctypes.c_int
     L.attn_int2_chunk_workspace.argtypes = [pL, i32, i32, i32]
     L.attn_int2_chunk_workspace.restype = sz
     L.attn_int2_chunk.argtypes = [pC, i32, vp, i32, i32, ctypes.c_float, vp, i32, vp, vp, sz, vp]
@@ -304,6 +308,22 @@ def attn_int2_decode(cache: KVCache, n_tokens: int, q: torch.Tensor, scale: floa
                                   _ptr(out), od, _ptr(lse), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)),
            "attn_int2_decode")
+    return out
+
+
+def attn_int2_decode_noalloc(cache: KVCache, n_tokens: int, q: torch.Tensor, scale: float,
+                             out: torch.Tensor, lse=None, stream=None) -> torch.Tensor:
+    """attn_int2_decode through the allocation-free entry point: the split
+    partials live in the library's fixed per-device scratch buffer, so the
+    call allocates nothing (out, and lse if wanted, are the caller's).
+    Calls that overlap on one device race on that buffer."""
+    out = _attention_io(cache, q, 3, (torch.float32, torch.bfloat16), out, None, lse, q.shape[:2])
+    qd = {torch.float32: F32, torch.bfloat16: BF16}[q.dtype]
+    od = {torch.float32: F32, torch.bfloat16: BF16}[out.dtype]
+    cs = cache.struct()
+    _check(lib().attn_int2_decode_noalloc(ctypes.byref(cs), int(n_tokens), _ptr(q), qd,
+                                          q.shape[1], float(scale), _ptr(out), od, _ptr(lse),
+                                          _stream(stream)), "attn_int2_decode_noalloc")
     return out
 
 

@@ -235,6 +235,20 @@ int attn_int2_decode(const kvq_cache* cache, int32_t n_tokens, const void* q, in
                                        out_dtype, lse, ws, (hipStream_t)stream));
 }
 
+int attn_int2_decode_noalloc(const kvq_cache* cache, int32_t n_tokens, const void* q,
+                             int32_t q_dtype, int32_t q_heads, float scale, void* out,
+                             int32_t out_dtype, float* lse, void* stream) {
+  int st = check_attention(cache, n_tokens, q, q_heads, out, out_dtype, lse);
+  if (st != KVQ_OK) return st;
+  if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return KVQ_EINVAL;
+  if (kvq::decode_workspace_bytes(&cache->layout, q_heads, n_tokens) > KVQ_NOALLOC_SCRATCH_BYTES)
+    return KVQ_ESCRATCH;
+  void* ws = nullptr;
+  if (kvq::decode_scratch(&ws) != hipSuccess || !ws) return KVQ_EHIP;
+  return hip_status(kvq::launch_decode(cache, n_tokens, q, q_dtype, q_heads, scale, out,
+                                       out_dtype, lse, ws, (hipStream_t)stream));
+}
+
 size_t attn_int2_chunk_workspace(const kvq_layout* L, int32_t q_len, int32_t q_heads,
                                  int32_t n_tokens) {
   if (check_layout(L) != KVQ_OK || q_heads < 1 || n_tokens < 1 || q_len < 1) return 0;
@@ -271,6 +285,7 @@ const char* kvq_status_string(int status) {
     case KVQ_ECAPACITY: return "exceeds cache capacity";
     case KVQ_EWORKSPACE: return "workspace missing or too small";
     case KVQ_EHIP: return "HIP launch error";
+    case KVQ_ESCRATCH: return "exceeds the fixed scratch buffer of the allocation-free decode";
     default: return "unknown status";
   }
 }

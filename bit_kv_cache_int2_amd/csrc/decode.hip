@@ -16,6 +16,8 @@
 // wave-shuffle maxima; each block merges its four waves and writes one
 // partial (o, m, l); a second kernel merges the splits, rotates rotated
 // values back and writes out/lse.
+#include <mutex>
+
 #include "code_operand.h"
 #include "device.h"
 #include "internal.h"
@@ -919,6 +921,35 @@ int decode_splits(const kvq_layout* L, int q_heads, int n_tokens) {
     }
   }
   return best;
+}
+
+// The split partials of attn_int2_decode_noalloc: a fixed device array,
+// one copy per device, kept until the process ends.  Its host-side name is
+// not a device address; the address on each device comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) float scratch[KVQ_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 size_t decode_workspace_bytes(const kvq_layout* L, int q_heads, int n_tokens) {

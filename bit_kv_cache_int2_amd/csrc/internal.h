@@ -47,6 +47,10 @@ hipError_t launch_decode(const kvq_cache* c, int n_tokens, const void* q,
                          int q_dtype, int q_heads, float scale, void* out,
                          int out_dtype, float* lse, void* ws, hipStream_t stream);
 
+// Device address of the fixed decode scratch buffer on the current device
+// (KVQ_NOALLOC_SCRATCH_BYTES bytes; looked up once per device).
+hipError_t decode_scratch(void** ptr);
+
 size_t chunk_workspace_bytes(const kvq_layout* L, int q_len, int q_heads,
                              int n_tokens);
 

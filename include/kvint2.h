@@ -6,7 +6,8 @@
  * current HIP device; `stream` is a hipStream_t passed as void* (NULL = the
  * default stream).  All calls only enqueue work on `stream` and return; a
  * return of KVQ_OK means "enqueued", not "finished".  The library allocates
- * nothing, keeps no state between calls and is safe to call from several
+ * nothing and keeps no state between calls (apart from the fixed scratch
+ * buffer of attn_int2_decode_noalloc), and is safe to call from several
  * host threads.  Every argument is checked on the host before anything is
  * launched: on any status other than KVQ_OK and KVQ_EHIP nothing was
  * launched and no output was touched.
@@ -56,7 +57,9 @@ enum {
   KVQ_EUNSUPPORTED = -2, /* valid but not built (e.g. head_dim 96)        */
   KVQ_ECAPACITY = -3,    /* tokens beyond the cache capacity              */
   KVQ_EWORKSPACE = -4,   /* workspace missing or too small                */
-  KVQ_EHIP = -5          /* the HIP runtime reported an error at launch   */
+  KVQ_EHIP = -5,         /* the HIP runtime reported an error at launch   */
+  KVQ_ESCRATCH = -6      /* needs more than the fixed scratch buffer of
+                            attn_int2_decode_noalloc                      */
 };
 
 /* ------------------------------------------------------------ modes */
@@ -294,6 +297,25 @@ int attn_int2_decode(const kvq_cache* cache, int32_t n_tokens,
                      float scale, void* out_dev, int32_t out_dtype,
                      float* lse_dev, void* ws_dev, size_t ws_bytes,
                      void* stream);
+
+/* ------------------------------------------------------------ no-alloc */
+/* attn_int2_decode for callers that cannot allocate device memory or pass
+ * a workspace: code under stream capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, kernels, results and errors as
+ * attn_int2_decode without ws_dev/ws_bytes: the split partials go to a
+ * fixed scratch buffer of KVQ_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on each device it runs on until the process ends (its address is
+ * looked up on the first call on a device).  Calls whose partials need
+ * more (attn_int2_decode_workspace() > KVQ_NOALLOC_SCRATCH_BYTES) return
+ * KVQ_ESCRATCH and launch nothing.  Every call on one device shares that
+ * buffer: calls that overlap on one device (on different streams, or from
+ * several host threads) race and give unspecified results; calls ordered
+ * on one stream are safe.  Nothing is allocated or freed. */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int attn_int2_decode_noalloc(const kvq_cache* cache, int32_t n_tokens,
+                             const void* q_dev, int32_t q_dtype, int32_t q_heads,
+                             float scale, void* out_dev, int32_t out_dtype,
+                             float* lse_dev, void* stream);
 
 /* ------------------------------------------------------------ chunk */
 /* Workspace bytes attn_int2_chunk needs for these sizes. */

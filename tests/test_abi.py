@@ -155,6 +155,29 @@ def test_attention_validation_without_launch():
                              p, 1 << 40, None) == kv.KVQ_EUNSUPPORTED
 
 
+def test_noalloc_decode_validation_without_launch():
+    """The allocation-free decode checks like attn_int2_decode and refuses,
+    before any launch, a call whose split partials exceed its fixed
+    scratch buffer."""
+    L = kv.lib()
+    p = ctypes.c_void_p(1 << 20)
+    c = _cache()
+    call = lambda cc=c, n=100, hq=8, od=kv.F32, qd=kv.F32: L.attn_int2_decode_noalloc(
+        ctypes.byref(cc), n, p, qd, hq, 0.1, p, od, None, None)
+    assert call(hq=6) == kv.KVQ_EINVAL
+    assert call(hq=12) == kv.KVQ_EUNSUPPORTED
+    assert call(n=0) == kv.KVQ_EINVAL
+    assert call(n=2000) == kv.KVQ_ECAPACITY
+    assert call(od=7) == kv.KVQ_EINVAL
+    assert call(qd=9) == kv.KVQ_EINVAL
+    assert L.attn_int2_decode_noalloc(None, 100, p, kv.F32, 8, 0.1, p, kv.F32, None, None) == kv.KVQ_EINVAL
+    big = _cache(batch=64, kv_heads=8, capacity=1 << 20)
+    need = L.attn_int2_decode_workspace(ctypes.byref(big.layout), 64, 1 << 20)
+    assert need > kv.NOALLOC_SCRATCH_BYTES
+    assert call(cc=big, n=1 << 20, hq=64) == kv.KVQ_ESCRATCH
+    assert L.kvq_status_string(kv.KVQ_ESCRATCH).startswith(b"exceeds the fixed scratch")
+
+
 def test_python_wrappers_check_shapes_before_any_call():
     """The bindings size-check what the C ABI cannot (q, out, lse against
     the layout) and raise ValueError before reaching the library; CPU
@@ -178,6 +201,8 @@ def test_python_wrappers_check_shapes_before_any_call():
         kv.attn_int2_decode(c, 100, q, 0.1, lse=torch.zeros((2, 4)))
     with pytest.raises(ValueError, match="lse must be one of"):
         kv.attn_int2_decode(c, 100, q, 0.1, lse=torch.zeros((2, 8), dtype=torch.float64))
+    with pytest.raises(ValueError, match="out must have shape"):
+        kv.attn_int2_decode_noalloc(c, 100, q, 0.1, out=torch.zeros((2, 8, 127)))
     qc = torch.zeros((2, 5, 8, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="q must be one of"):
         kv.attn_int2_chunk(c, 100, qc.float(), 0.1)
