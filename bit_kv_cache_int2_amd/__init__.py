@@ -26,14 +26,14 @@ KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ECAPACITY, KVQ_EWORKSPACE, KVQ_EHIP = 
 KVQ_ESCRATCH = -6
 NOALLOC_SCRATCH_BYTES = 16 << 20   # KVQ_NOALLOC_SCRATCH_BYTES
 KEY_WINDOW, KEY_CENTROID, KEY_CENTROID_QSAC = 0, 1, 2
-VAL_GROUP, VAL_HADAMARD = 0, 1
+VAL_GROUP, VAL_HADAMARD, VAL_HADAMARD_MODAL = 0, 1, 2
 F32, BF16 = 0, 1
 QSAC_EXACT, QSAC_RANGE = 0, 1     # QSAC perturbation estimate
 PSAC_F16, PSAC_INT8 = 0, 1        # PSAC coefficient storage
 GROUP, WINDOW = 32, 64
 
 BUFFERS = ("k_codes", "k_params", "k_tail", "k_idx", "centroids", "sens_w", "psac_basis",
-           "k_psac", "v_codes", "v_params")
+           "k_psac", "v_codes", "v_params", "v_signs", "v_modality")
 
 
 class KVQError(RuntimeError):
@@ -47,7 +47,8 @@ class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("batch", "kv_heads", "head_dim", "capacity",
                                                "key_mode", "value_mode", "n_centroids",
                                                "qsac_topk", "psac_rank", "qsac_score",
-                                               "psac_format", "centroid_key_split")]
+                                               "psac_format", "centroid_key_split",
+                                               "n_modalities")]
 
 
 class CacheStruct(ctypes.Structure):
@@ -169,18 +170,21 @@ class KVCache:
     bytes viewed as k_psac8 i8 [B,H,T,R] and k_psac_sc i16 (fp16 bits)
     [B,H,T]; v_codes u8 [B,H,T/64,D,16] (per 64-token tile, channel-major:
     token t of the tile, channel c in byte 16c + t/4, bits 2(t%4));
-    v_params i32 [B,H,T,D/32].
-    Calibration inputs (centroids, sens_w, psac_basis) are filled by the caller.
+    v_params i32 [B,H,T,D/32]; with value_mode VAL_HADAMARD_MODAL, v_signs i32
+    [H,M,D/32] (sign bits of each head's per-modality rotation, bit c % 32 of
+    word c / 32 set = -1) and v_modality u8 [B,T] (modality of each token).
+    Calibration inputs (centroids, sens_w, psac_basis) and the modal inputs
+    (v_signs, and v_modality before each append) are filled by the caller.
     """
 
     def __init__(self, batch: int, kv_heads: int, head_dim: int, capacity: int,
                  key_mode: int = KEY_WINDOW, value_mode: int = VAL_GROUP,
                  n_centroids: int = 0, qsac_topk: int = 1, psac_rank: int = 0,
                  qsac_score: int = QSAC_EXACT, psac_format: int = PSAC_F16,
-                 centroid_key_split: bool = False, device="cuda"):
+                 centroid_key_split: bool = False, n_modalities: int = 1, device="cuda"):
         self.layout = Layout(batch, kv_heads, head_dim, capacity, key_mode, value_mode,
                              n_centroids, qsac_topk, psac_rank, qsac_score, psac_format,
-                             int(bool(centroid_key_split)))
+                             int(bool(centroid_key_split)), int(n_modalities))
         _check(lib().kvq_layout_check(ctypes.byref(self.layout)), "layout")
         B, H, D, T = batch, kv_heads, head_dim, capacity
         shapes = {
@@ -197,6 +201,8 @@ class KVCache:
                        torch.uint8 if psac_format == PSAC_INT8 else torch.int16),
             "v_codes": ((B, H, T // WINDOW, D, 16), torch.uint8),
             "v_params": ((B, H, T, D // GROUP), torch.int32),
+            "v_signs": ((H, max(n_modalities, 1), D // 32), torch.int32),
+            "v_modality": ((B, T), torch.uint8),
         }
         self.buffers = {}
         for i, name in enumerate(BUFFERS):

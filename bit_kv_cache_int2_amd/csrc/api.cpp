@@ -19,7 +19,11 @@ int check_layout(const kvq_layout* L) {
       L->capacity % KVQ_WINDOW != 0)
     return KVQ_EINVAL;
   if (L->key_mode < KVQ_KEY_WINDOW || L->key_mode > KVQ_KEY_CENTROID_QSAC) return KVQ_EINVAL;
-  if (L->value_mode != KVQ_VAL_GROUP && L->value_mode != KVQ_VAL_HADAMARD) return KVQ_EINVAL;
+  if (L->value_mode != KVQ_VAL_GROUP && L->value_mode != KVQ_VAL_HADAMARD &&
+      L->value_mode != KVQ_VAL_HADAMARD_MODAL)
+    return KVQ_EINVAL;
+  if (L->value_mode == KVQ_VAL_HADAMARD_MODAL && (L->n_modalities < 1 || L->n_modalities > 3))
+    return KVQ_EUNSUPPORTED;
   if (L->head_dim != 64 && L->head_dim != 128) return KVQ_EUNSUPPORTED;
   if (L->key_mode != KVQ_KEY_WINDOW) {
     if (L->n_centroids < 1 || L->n_centroids > 256) return KVQ_EUNSUPPORTED;
@@ -58,6 +62,8 @@ bool uses(const kvq_layout* L, int which) {
     case KVQ_BUF_SENS_W: return L->key_mode == KVQ_KEY_CENTROID_QSAC;
     case KVQ_BUF_PSAC_BASIS:
     case KVQ_BUF_K_PSAC: return !win && L->psac_rank > 0;
+    case KVQ_BUF_V_SIGNS:
+    case KVQ_BUF_V_MODALITY: return L->value_mode == KVQ_VAL_HADAMARD_MODAL;
     default: return false;
   }
 }
@@ -74,6 +80,8 @@ const void* buf(const kvq_cache* c, int which) {
     case KVQ_BUF_K_PSAC: return c->k_psac;
     case KVQ_BUF_V_CODES: return c->v_codes;
     case KVQ_BUF_V_PARAMS: return c->v_params;
+    case KVQ_BUF_V_SIGNS: return c->v_signs;
+    case KVQ_BUF_V_MODALITY: return c->v_modality;
     default: return nullptr;
   }
 }
@@ -145,6 +153,8 @@ size_t kvq_buffer_bytes(const kvq_layout* L, int32_t which) {
       return L->key_mode == KVQ_KEY_WINDOW ? BH * (T / KVQ_WINDOW) * D * 4
                                            : BH * T * (D / KVQ_GROUP) * 4;
     case KVQ_BUF_V_PARAMS: return BH * T * (D / KVQ_GROUP) * 4;
+    case KVQ_BUF_V_SIGNS: return (size_t)L->kv_heads * L->n_modalities * (D / 32) * 4;
+    case KVQ_BUF_V_MODALITY: return (size_t)L->batch * T;
     case KVQ_BUF_K_TAIL: return BH * KVQ_WINDOW * D * 2;
     case KVQ_BUF_K_IDX: return BH * T;
     case KVQ_BUF_CENTROIDS: return BH * (size_t)L->n_centroids * D * 4;

@@ -11,7 +11,9 @@
 //    (q.C)[idx] + sum_g s_g (q_g . codes_g) + z_g sum(q_g) [+ (U^T q) . a];
 //  * values: p~ = p * s_(t,g) goes through LDS, each lane reads its channels'
 //    64-token code rows straight from the channel-major value tile, and the z
-//    part is a per-lane running sum sum_t p_t z_(t,g).
+//    part is a per-lane running sum sum_t p_t z_(t,g).  With per-modality
+//    rotations each code takes the sign of its (token modality, channel) and
+//    the z part is summed per modality, signed per channel at the end.
 // The online softmax works in base 2 (logits pre-scaled by log2 e) with
 // wave-shuffle maxima; each block merges its four waves and writes one
 // partial (o, m, l); a second kernel merges the splits, rotates rotated
@@ -64,16 +66,19 @@ struct DecodeArgs {
   const uint16_t* kpsac_sc;   // INT8: per-token fp16 scales
   const uint8_t* vcodes;
   const uint32_t* vparams;
+  const uint32_t* vsigns;     // per-modality rotations: [H][M][D/32] sign bits
+  const uint8_t* vmodal;      // per-modality rotations: [B][Tcap] modality ids
   const void* q;
   float* ws;
-  int q_bf16, H, Hq, Tcap, C, n_tokens, split_len, S, psac_int8;
+  int q_bf16, H, Hq, Tcap, C, n_tokens, split_len, S, psac_int8, M;
   float scale_log2;
 };
 
-template <int D, int G, int KM, int R>
+template <int D, int G, int KM, int R, bool MOD>
 __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a) {
   constexpr int NG = D / kGroup;      // parameter groups per row
   constexpr int CPL = D / kWave;      // P.V channels per lane
+  constexpr int NM = MOD ? 3 : 1;     // modality z sums kept per lane
   __shared__ float qs[D][G];
   __shared__ float qc[KM == 1 ? G : 1][KM == 1 ? 256 : 1];
   __shared__ float qsum[G][NG];
@@ -125,13 +130,28 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
   const int n_full_win = a.n_tokens / kWindow;
   const int w_begin = t_begin / kWindow, w_end = (t_end + kWindow - 1) / kWindow;
 
-  float m_run[G], l_lane[G], pz[G][NG], o[G][CPL];
+  // per-modality rotations: bit m of csgn[c] = sign of channel lane*CPL + c
+  // in modality m
+  uint32_t csgn[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    csgn[c] = 0u;
+    if (MOD) {
+      const int ch = lane * CPL + c;
+      for (int m = 0; m < a.M; ++m)
+        csgn[c] |= ((a.vsigns[((int64_t)h * a.M + m) * (D / 32) + ch / 32] >> (ch & 31)) & 1u) << m;
+    }
+  }
+
+  float m_run[G], l_lane[G], pz[G][NM][NG], o[G][CPL];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m_run[g] = -__builtin_inff();
     l_lane[g] = 0.0f;
 #pragma unroll
-    for (int gr = 0; gr < NG; ++gr) pz[g][gr] = 0.0f;
+    for (int mm = 0; mm < NM; ++mm)
+#pragma unroll
+      for (int gr = 0; gr < NG; ++gr) pz[g][mm][gr] = 0.0f;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) o[g][c] = 0.0f;
   }
@@ -259,9 +279,13 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
 #pragma unroll
       for (int c = 0; c < CPL; ++c) o[g][c] *= alpha;
 #pragma unroll
-      for (int gr = 0; gr < NG; ++gr) pz[g][gr] *= alpha;
+      for (int mm = 0; mm < NM; ++mm)
+#pragma unroll
+        for (int gr = 0; gr < NG; ++gr) pz[g][mm][gr] *= alpha;
       m_run[g] = mn;
     }
+    // this lane's token's modality (per-modality rotations)
+    const int mt = MOD ? min((int)a.vmodal[(int64_t)b * a.Tcap + min(t, a.n_tokens - 1)], a.M - 1) : 0;
 
     // ---- values: p~ through LDS; each lane reads its channels' tile rows
     {
@@ -281,7 +305,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
         for (int g = 0; g < G; ++g) {
           const float pg = valid ? p[g] : 0.0f;
           pt[wave][lane][gr][g] = pg * sc;
-          pz[g][gr] = __builtin_fmaf(pg, zc, pz[g][gr]);
+#pragma unroll
+          for (int mm = 0; mm < NM; ++mm)
+            pz[g][mm][gr] = __builtin_fmaf((mm == mt) ? pg : 0.0f, zc, pz[g][mm][gr]);
         }
       }
     }
@@ -298,10 +324,13 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
             a.vcodes + ((bh * (a.Tcap / kWindow) + win) * D + c0 + c) * 16);
       for (int tt = 0; tt < kWave; ++tt) {
         float cf[CPL];
+        // modality of token tt (wave-uniform): that of lane tt
+        const int mtt = MOD ? __builtin_amdgcn_readlane(mt, tt) : 0;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
           const uint32_t wd = (tt < 16) ? crow[c].x : (tt < 32) ? crow[c].y : (tt < 48) ? crow[c].z : crow[c].w;
           cf[c] = (float)((wd >> (2 * (tt & 15))) & 3u);
+          if (MOD) cf[c] = __uint_as_float(__float_as_uint(cf[c]) ^ (((csgn[c] >> mtt) & 1u) << 31));
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -321,11 +350,19 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float l = wave_sum(l_lane[g]);
-      float zsum[NG];
+      float zsum[NM][NG];
 #pragma unroll
-      for (int q = 0; q < NG; ++q) zsum[q] = wave_sum(pz[g][q]);
+      for (int mm = 0; mm < NM; ++mm)
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) wo[wave][g][c0 + c] = o[g][c] + zsum[gr];
+        for (int q = 0; q < NG; ++q) zsum[mm][q] = wave_sum(pz[g][mm][q]);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        float zc = 0.0f;
+#pragma unroll
+        for (int mm = 0; mm < NM; ++mm)
+          zc += ((csgn[c] >> mm) & 1u) ? -zsum[mm][gr] : zsum[mm][gr];
+        wo[wave][g][c0 + c] = o[g][c] + zc;
+      }
       if (lane == 0) {
         wm[wave][g] = m_run[g];
         wlv[wave][g] = l;
@@ -860,7 +897,8 @@ __global__ __launch_bounds__(128) void decode_reduce_kernel(const float* __restr
 template <int D, int G, int KM, int R>
 hipError_t launch_partial(const DecodeArgs& a, int B, hipStream_t st) {
   const dim3 grid((unsigned)a.S, (unsigned)a.H, (unsigned)B);
-  decode_partial_kernel<D, G, KM, R><<<grid, 256, 0, st>>>(a);
+  if (a.vmodal) decode_partial_kernel<D, G, KM, R, true><<<grid, 256, 0, st>>>(a);
+  else decode_partial_kernel<D, G, KM, R, false><<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -874,7 +912,7 @@ hipError_t launch_partial_mode(const DecodeArgs& a, int key_mode, int R, int B, 
 template <int D>
 hipError_t launch_partial_g(const DecodeArgs& a, int G, int key_mode, int R, int B,
                             hipStream_t st) {
-  if (D == 128 && G == 4 && key_mode == KVQ_KEY_WINDOW) {
+  if (D == 128 && G == 4 && key_mode == KVQ_KEY_WINDOW && !a.vmodal) {
     const dim3 grid((unsigned)a.S, (unsigned)a.H, (unsigned)B);
     decode_mfma_kernel<<<grid, 256, 0, st>>>(a);
     return hipGetLastError();
@@ -979,6 +1017,10 @@ hipError_t launch_decode(const kvq_cache* c, int n_tokens, const void* q, int q_
                            : nullptr;
   a.vcodes = (const uint8_t*)c->v_codes;
   a.vparams = (const uint32_t*)c->v_params;
+  const bool modal = L.value_mode == KVQ_VAL_HADAMARD_MODAL;
+  a.vsigns = modal ? (const uint32_t*)c->v_signs : nullptr;
+  a.vmodal = modal ? (const uint8_t*)c->v_modality : nullptr;
+  a.M = modal ? L.n_modalities : 1;
   a.q = q;
   a.ws = (float*)ws;
   a.q_bf16 = (q_dtype == KVQ_BF16);
@@ -997,7 +1039,7 @@ hipError_t launch_decode(const kvq_cache* c, int n_tokens, const void* q, int q_
                      : launch_partial_g<64>(a, G, L.key_mode, R, L.batch, stream);
   if (e != hipSuccess) return e;
   const int BHq = L.batch * q_heads;
-  const bool had = L.value_mode == KVQ_VAL_HADAMARD;
+  const bool had = L.value_mode != KVQ_VAL_GROUP;
   const int ob = out_dtype == KVQ_BF16;
   if (L.head_dim == 128) {
     if (had) decode_reduce_kernel<128, true><<<BHq, 128, 0, stream>>>((const float*)ws, S, BHq, out, ob, lse);

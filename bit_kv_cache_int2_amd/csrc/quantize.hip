@@ -1,6 +1,7 @@
 // Quantise-append into the packed INT2 cache.
 //
-//  * values ([OKV] rotated values, optional) and window keys ([OKV]
+//  * values ([OKV] rotated values, optional, separately per modality) and
+//    window keys ([OKV]
 //    per-window key ranges): one block per (head, 64-token tile, sequence),
 //    see tile_append_kernel.  A token row sits in D/8 lanes, 8 channels (16
 //    bytes of bf16) per lane, so a 32-channel parameter group is one lane
@@ -93,12 +94,16 @@ KVQ_DEV void wht_row(float (&x)[8]) {
 //    per channel derives the thresholds, and every thread packs the codes of
 //    its own slices.  Block 0 also writes the tokens of the window left
 //    unfinished into the tail, after every thread has read the old tail.
-template <int D, bool HAD, bool KEYS>
+// VM: 0 plain values, 1 rotated, 2 rotated per modality (the rotated row
+// with the channels whose sign is -1 in the token's modality negated).
+template <int D, int VM, bool KEYS>
 __global__ __launch_bounds__(256) void tile_append_kernel(
     const uint16_t* __restrict__ kin, const uint16_t* __restrict__ vin,
     uint8_t* __restrict__ kcodes, uint32_t* __restrict__ kparams,
     uint16_t* __restrict__ ktail, uint8_t* __restrict__ vcodes,
-    uint32_t* __restrict__ vparams, int H, int Tcap, int cur_len, int n_new) {
+    uint32_t* __restrict__ vparams, int H, int Tcap, int cur_len, int n_new,
+    const uint32_t* __restrict__ vsigns, const uint8_t* __restrict__ vmodal, int M) {
+  constexpr bool HAD = VM != 0;
   constexpr int LPR = D / 8, RPP = 256 / LPR, NP = kWindow / RPP;
   __shared__ float red_mn[4][D], red_mx[4][D];
   __shared__ float thr[3][D];   // negated key thresholds per channel
@@ -127,11 +132,17 @@ __global__ __launch_bounds__(256) void tile_append_kernel(
   // unspecified, or none at all.
   const int64_t row0 = ((int64_t)b * n_new - cur_len) * H + h;   // row index of token p: row0 + p * H
   uint4 vraw[NP], kraw[NP];
+  uint32_t vneg[NP];   // per-modality rotations: sign bits of this row's 8 channels
 #pragma unroll
   for (int k = 0; k < NP; ++k) {
     const int p = wb + r0 + RPP * k;
     const int pc = min(max(p, t_lo), t_hi - 1);
     vraw[k] = ld_stream(vin + (row0 + (int64_t)pc * H) * D + j * 8);
+    vneg[k] = 0u;
+    if (VM == 2) {
+      const int m = min((int)vmodal[(int64_t)b * Tcap + pc], M - 1);
+      vneg[k] = (vsigns[((int64_t)h * M + m) * (D / 32) + (8 * j) / 32] >> ((8 * j) & 31)) & 0xFFu;
+    }
     const int pk = full ? p : pc;
     const uint16_t* src = (pk < cur_len) ? tail + (int64_t)(pk & (kWindow - 1)) * D
                                          : kin + (row0 + (int64_t)pk * H) * D;
@@ -161,6 +172,10 @@ __global__ __launch_bounds__(256) void tile_append_kernel(
     float x[8];
     bf16x8_to_f32(vraw[k], x);
     if (HAD) wht_row<D>(x);
+    if (VM == 2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(__float_as_uint(x[e]) ^ (((vneg[k] >> e) & 1u) << 31));
+    }
     float mn = x[0], mx = x[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) {
@@ -298,10 +313,12 @@ hipError_t launch_tile_append(const kvq_cache* c, const void* k, const void* v, 
     kern<<<grid, 256, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, (uint8_t*)c->k_codes,
                                (uint32_t*)c->k_params, (uint16_t*)c->k_tail,
                                (uint8_t*)c->v_codes, (uint32_t*)c->v_params, L.kv_heads,
-                               L.capacity, cur_len, n_new);
+                               L.capacity, cur_len, n_new, (const uint32_t*)c->v_signs,
+                               (const uint8_t*)c->v_modality, L.n_modalities);
   };
-  if (L.value_mode == KVQ_VAL_HADAMARD) args(tile_append_kernel<D, true, KEYS>);
-  else args(tile_append_kernel<D, false, KEYS>);
+  if (L.value_mode == KVQ_VAL_HADAMARD_MODAL) args(tile_append_kernel<D, 2, KEYS>);
+  else if (L.value_mode == KVQ_VAL_HADAMARD) args(tile_append_kernel<D, 1, KEYS>);
+  else args(tile_append_kernel<D, 0, KEYS>);
   return hipGetLastError();
 }
 

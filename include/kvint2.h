@@ -87,7 +87,15 @@ enum {
    * head_dim (Sylvester order, stages 1,2,4,.. in fp32, then times
    * fp32(1/sqrt(head_dim))) is applied before quantisation; attention
    * outputs are rotated back. */
-  KVQ_VAL_HADAMARD = 1
+  KVQ_VAL_HADAMARD = 1,
+  /* [OKV] values rotated separately per modality: token t of modality
+   * m = v_modality[b][t] is rotated by R_m = diag(sigma_m) H, H the
+   * Walsh-Hadamard transform above and sigma_m in {+1,-1}^head_dim the
+   * sign vector of (kv head, modality m) in v_signs; i.e. the rotated row
+   * of the KVQ_VAL_HADAMARD mode with the channels whose sign is -1
+   * negated.  Attention rotates back with R_m^T = H diag(sigma_m).  With
+   * every sign +1 this is KVQ_VAL_HADAMARD. */
+  KVQ_VAL_HADAMARD_MODAL = 2
 };
 
 /* QSAC perturbation estimate (kvq_layout.qsac_score) */
@@ -134,10 +142,10 @@ typedef struct kvq_layout {
                           centroid modes only                          */
   int32_t qsac_score;  /* KVQ_QSAC_* (QSAC only; else ignored)         */
   int32_t psac_format; /* KVQ_PSAC_* (psac_rank > 0; else ignored)     */
-  int32_t centroid_key_split; /* chunk attention over centroid keys: 0 =
-                         one fp16 copy per key element (default), 1 = fp16
-                         hi + lo, exact to fp32 like window keys and about a
-                         third slower; 0 or 1 (centroid modes; else ignored) */
+  int32_t centroid_key_split; /* 0 or 1, accepted and ignored: chunk
+                         attention enters every key as fp16 hi + lo (kept
+                         for layout compatibility)                     */
+  int32_t n_modalities; /* M, 1..3 (KVQ_VAL_HADAMARD_MODAL; else ignored) */
 } kvq_layout;
 
 /* Device buffers of one layer's packed cache.  Shapes are C order.
@@ -165,6 +173,13 @@ typedef struct kvq_layout {
  *                                      codes are contiguous, as the
  *                                      token-axis reduction of P.V reads them
  *   v_params   u32 [B][H][Tcap][D/32]
+ *   v_signs    u32 [H][M][D/32]        caller-filled (KVQ_VAL_HADAMARD_MODAL):
+ *                                      sigma of (head h, modality m), bit
+ *                                      c % 32 of word c / 32 set = -1
+ *   v_modality u8  [B][Tcap]           caller-filled (KVQ_VAL_HADAMARD_MODAL):
+ *                                      modality (0..M-1) of each token, written
+ *                                      before the token is appended and kept
+ *                                      (an id >= M is read as M - 1)
  * Buffers a mode does not use may be NULL.  Rows of tokens in an
  * unfinished window and tail slots at or beyond (length % 64) hold
  * unspecified bytes (for values: the bits of tokens at or beyond the length in
@@ -181,6 +196,8 @@ typedef struct kvq_cache {
   void* k_psac;
   void* v_codes;
   void* v_params;
+  const void* v_signs;
+  const void* v_modality;
 } kvq_cache;
 
 enum {
@@ -194,6 +211,8 @@ enum {
   KVQ_BUF_K_PSAC,
   KVQ_BUF_V_CODES,
   KVQ_BUF_V_PARAMS,
+  KVQ_BUF_V_SIGNS,
+  KVQ_BUF_V_MODALITY,
   KVQ_BUF_COUNT
 };
 
@@ -281,7 +300,7 @@ size_t attn_int2_decode_workspace(const kvq_layout* L, int32_t q_heads,
  * inside attention; no dense cache is built).  q_dev [B][q_heads][D] in
  * q_dtype (KVQ_F32 or KVQ_BF16); query head h reads kv head
  * h / (q_heads / H).  out_dev [B][q_heads][D] in out_dtype, rotated back
- * to the input basis for KVQ_VAL_HADAMARD; lse_dev (nullable) f32
+ * to the input basis for the rotated value modes; lse_dev (nullable) f32
  * [B][q_heads] = log sum_t exp(scale * logit_t).  Logits include the PSAC
  * term (U^T q) . a_t when psac_rank > 0.  No mask.  ws_dev: scratch of
  * attn_int2_decode_workspace() bytes.
@@ -328,16 +347,14 @@ size_t attn_int2_chunk_workspace(const kvq_layout* L, int32_t q_len,
  * [B][q_len][q_heads][D] in out_dtype; lse_dev (nullable) f32
  * [B][q_heads][q_len].  Every query row sees every cached token (no mask);
  * the chunk's own keys/values are not included -- merge them with lse.
- * Precision: fp16 MFMA operands with fp32 accumulation.  Window keys enter
- * as fp16 hi + lo (exact to fp32); a centroid key enters as one fp16 value
- * per element (centroid + residual summed in fp32, rounded once), so each
- * logit term carries a relative error of up to 2^-11: within 2e-3 of the
- * exact attention for keys near unit rms, growing with the key magnitudes
- * beyond that, unless the layout sets centroid_key_split (hi + lo for
- * centroid keys too).  Probabilities and dequantised values enter as one
- * fp16 each: an error near 2^-11 max|v| where a few tokens carry the
- * softmax (2e-3 is reached for values near 8).  Same window-key contract
- * on n_tokens and same errors as attn_int2_decode. */
+ * Precision: fp16 MFMA operands with fp32 accumulation.  Every key enters
+ * as fp16 hi + lo (exact to fp32), the PSAC term as hi/lo parts too; a
+ * value enters as (code - 1) s, exact in fp16, with z + s of its group
+ * summed exactly by one more MFMA; probabilities are fp16 (their rounding
+ * multiplies v - o).  Within 2e-3 of the exact attention for keys with
+ * per-channel scales to 5 and values with peaks near 12 (the tests).
+ * Same window-key contract on n_tokens and same errors as
+ * attn_int2_decode. */
 int attn_int2_chunk(const kvq_cache* cache, int32_t n_tokens,
                     const void* q_bf16_dev, int32_t q_len, int32_t q_heads,
                     float scale, void* out_dev, int32_t out_dtype,

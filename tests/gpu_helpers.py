@@ -34,20 +34,26 @@ def to_oracle(c: kv.KVCache) -> oracle.Cache:
                         k_psac=None if int8 else get("k_psac", np.uint16),
                         k_psac8=get("k_psac8", np.int8) if int8 else None,
                         k_psac_sc=get("k_psac_sc", np.uint16) if int8 else None,
-                        v_codes=get("v_codes", np.uint8), v_params=get("v_params", np.uint32))
+                        v_codes=get("v_codes", np.uint8), v_params=get("v_params", np.uint32),
+                        M=L.n_modalities if L.value_mode == kv.VAL_HADAMARD_MODAL else 1,
+                        v_signs=get("v_signs", np.uint32), v_modal=get("v_modality", np.uint8))
 
 
 def oracle_like(c: kv.KVCache) -> oracle.Cache:
     """An empty oracle cache with the same layout and calibration inputs."""
     L = c.layout
     o = oracle.Cache(L.batch, L.kv_heads, L.head_dim, L.capacity, L.key_mode, L.value_mode,
-                     L.n_centroids, L.qsac_topk, L.psac_rank, L.qsac_score, L.psac_format)
+                     L.n_centroids, L.qsac_topk, L.psac_rank, L.qsac_score, L.psac_format,
+                     M=L.n_modalities if L.value_mode == kv.VAL_HADAMARD_MODAL else 1)
     if c.centroids is not None:
         o.centroids[:] = host(c.centroids, np.float32)
     if c.sens_w is not None:
         o.sens_w[:] = host(c.sens_w, np.float32)
     if c.psac_basis is not None:
         o.psac_basis[:] = host(c.psac_basis, np.float32)
+    if c.v_signs is not None:
+        o.v_signs[:] = host(c.v_signs, np.uint32)
+        o.v_modal[:] = host(c.v_modality, np.uint8)
     return o
 
 

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 def _layout(**kw):
     d = dict(batch=2, kv_heads=4, head_dim=128, capacity=1024, key_mode=kv.KEY_WINDOW,
              value_mode=kv.VAL_GROUP, n_centroids=0, qsac_topk=1, psac_rank=0, qsac_score=0,
-             psac_format=0, centroid_key_split=0)
+             psac_format=0, centroid_key_split=0, n_modalities=1)
     d.update(kw)
     return kv.Layout(*[d[f] for f, _ in kv.Layout._fields_])
 
@@ -72,6 +72,12 @@ def test_layout_validation():
     assert chk(batch=65535, kv_heads=1, capacity=64) == kv.KVQ_OK
     assert chk(batch=65536, kv_heads=1, capacity=64) == kv.KVQ_EUNSUPPORTED
     assert chk(batch=1, kv_heads=65536, capacity=64) == kv.KVQ_EUNSUPPORTED
+    # per-modality rotations: 1..3 modalities
+    assert chk(value_mode=kv.VAL_HADAMARD_MODAL, n_modalities=3) == kv.KVQ_OK
+    assert chk(value_mode=kv.VAL_HADAMARD_MODAL, n_modalities=0) == kv.KVQ_EUNSUPPORTED
+    assert chk(value_mode=kv.VAL_HADAMARD_MODAL, n_modalities=4) == kv.KVQ_EUNSUPPORTED
+    assert chk(value_mode=3) == kv.KVQ_EINVAL
+    assert chk(n_modalities=9) == kv.KVQ_OK                # ignored without the modal mode
 
 
 def test_buffer_sizes():
@@ -92,6 +98,9 @@ def test_buffer_sizes():
                 psac_format=kv.PSAC_INT8)
     assert nb(7) == BH * T * 10
     assert nb(99) == 0
+    assert nb(10) == 0 and nb(11) == 0
+    L = _layout(value_mode=kv.VAL_HADAMARD_MODAL, n_modalities=3)
+    assert nb(10) == 4 * 3 * (D // 32) * 4 and nb(11) == 2 * T
 
 
 def _cache(**kw):

@@ -1,7 +1,8 @@
 """Seeded random configurations through the whole path: quantize-append in
 one to three calls, decode and chunk attention, against the oracle.  Each
 case draws the key mode (window, centroid, QSAC with the exact or the range
-estimate), the value mode (plain or rotated), head_dim 64 / 128, PSAC off /
+estimate), the value mode (plain, rotated, or rotated per modality with
+one to three modalities), head_dim 64 / 128, PSAC off /
 fp16 / INT8, batch, heads, GQA, the centroid count (1 .. 256), ragged
 lengths and capacities, and the query dtype.  Caches must match bit for bit;
 attention within 2e-3.  A draw that failed once is fixed in the code, not
@@ -28,7 +29,7 @@ CASES = int(os.environ.get("KVQ_SWEEP_CASES", "300"))   # more for a deeper one-
 def _draw(case: int, seed0: int = 9000, t_range=(1, 700), lq_range=(1, 150), g_choices=(1, 2, 4)):
     r = np.random.default_rng(seed0 + case)
     cfg = dict(D=int(r.choice([64, 128])), key_mode=int(r.integers(0, 3)),
-               value_mode=int(r.integers(0, 2)), B=int(r.integers(1, 3)), H=int(r.integers(1, 4)),
+               value_mode=int(r.integers(0, 3)), B=int(r.integers(1, 3)), H=int(r.integers(1, 4)),
                G=int(r.choice(list(g_choices))), T=int(r.integers(*t_range)))
     cfg["cap_extra"] = int(r.integers(0, 2)) * 64
     centroid = cfg["key_mode"] != kv.KEY_WINDOW
@@ -43,6 +44,7 @@ def _draw(case: int, seed0: int = 9000, t_range=(1, 700), lq_range=(1, 150), g_c
     cfg["Lq"] = int(r.integers(*lq_range))
     cfg["q_f32"] = bool(r.random() < 0.5)
     cfg["split"] = bool(centroid and r.random() < 0.5)
+    cfg["M"] = int(r.integers(1, 4)) if cfg["value_mode"] == kv.VAL_HADAMARD_MODAL else 1
     return cfg, r
 
 
@@ -79,25 +81,24 @@ def _run(cfg, r, name, chunk_rows=None):
     D, B, H, T, G = cfg["D"], cfg["B"], cfg["H"], cfg["T"], cfg["G"]
     Hq = H * G
     tag = f"{name}: {cfg}"
-    # keys: per-channel scales and offsets (window ranges and residuals both
-    # see spread).  Window keys take a wide spread (rms about 2.4, peaks near
-    # 20); centroid keys stay near the unit rms of the centroid workloads,
-    # the range in which one fp16 copy of each dequantised key keeps chunk
-    # attention within the tolerance (beyond it, test_gpu_chunk checks the
-    # chunk path against attention over fp16-rounded keys)
-    # (centroid keys split hi + lo take the wide spread too)
-    top, spread = (5.0, 1.5) if cfg["key_mode"] == kv.KEY_WINDOW or cfg["split"] else (2.0, 0.5)
-    sc = np.exp(r.uniform(np.log(0.2), np.log(top), (1, 1, H, D)))
-    off = r.normal(0, spread, (1, 1, H, D))
+    # keys: per-channel scales to 5 and offsets of sd 1.5 (rms about 2.4,
+    # peaks near 20) for every key mode, so window ranges and centroid
+    # residuals both see spread; values at 0.5 to 2 times unit scale
+    # (peaks to about 9)
+    sc = np.exp(r.uniform(np.log(0.2), np.log(5.0), (1, 1, H, D)))
+    off = r.normal(0, 1.5, (1, 1, H, D))
     K = synth.to_bf16_bits((r.standard_normal((B, T, H, D)) * sc + off).astype(np.float32))
-    # values at 0.5 to 1.5 times the workloads' unit scale: attention rounds
-    # its probability and value operands to fp16, an error near 2^-11 max|v|
-    # when a few tokens carry the softmax, which reaches 2e-3 for |v| near 8
-    V = synth.to_bf16_bits((r.standard_normal((B, T, H, D)) * r.uniform(0.5, 1.5)).astype(np.float32))
+    V = synth.to_bf16_bits((r.standard_normal((B, T, H, D)) * r.uniform(0.5, 2.0)).astype(np.float32))
     cap = ((T + 63) // 64) * 64 + cfg["cap_extra"]
     c = kv.KVCache(B, H, D, cap, key_mode=cfg["key_mode"], value_mode=cfg["value_mode"],
                    n_centroids=cfg["C"], qsac_topk=cfg["topk"], psac_rank=cfg["R"],
-                   qsac_score=cfg["score"], psac_format=cfg["fmt"], centroid_key_split=cfg["split"])
+                   qsac_score=cfg["score"], psac_format=cfg["fmt"], centroid_key_split=cfg["split"],
+                   n_modalities=cfg["M"])
+    if c.v_signs is not None:          # per-modality rotations: random signs and modality runs
+        c.v_signs.copy_(torch.from_numpy(
+            r.integers(0, 1 << 32, size=(H, cfg["M"], D // 32), dtype=np.uint64).astype(np.uint32).view(np.int32)))
+        runs = np.repeat(r.integers(0, cfg["M"], size=cap // 16 + 1), 16)[:cap]
+        c.v_modality.copy_(torch.from_numpy(np.tile(runs.astype(np.uint8), (B, 1))))
     if c.centroids is not None:        # calibration inputs: keys picked at random, weights, a basis
         Kf = synth.bf16_bits_to_f32(K)
         cent = np.stack([np.stack([Kf[b, r.integers(0, T, cfg["C"]), h] for h in range(H)])
