@@ -95,12 +95,52 @@ KVQ_DEV float fma_code(uint32_t word, bool hi, float s, float zc) {
   return __builtin_fmaf((float)c, s, zc);
 }
 
-// Position of tile token t (0..63) in the PV operand's k order: k-step
-// t / 32; inside it, lane group g' supplies tokens 4g' .. 4g'+3 and
-// 16 + 4g' .. 16 + 4g'+3 at positions 8g' .. 8g'+7.
+// fp16(x0 - lo half of hi), fp16(x1 - high half of hi): the lo parts of an
+// fp16 hi + lo split, each one fused multiply-add (exact in fp32) rounded
+// once to nearest, written straight into the two halves of the result.
+KVQ_DEV uint32_t lo_pair(uint32_t hi, float x0, float x1) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, -%1, 1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "=&v"(r)
+      : "v"(hi), "v"(x0), "v"(x1));
+  return r;
+}
+
+// (code - 1) s for the two codes of an operand dword (base + code in each
+// half) and the two scales of s2; nb holds -(base + 1) in both halves.  The
+// sum leaves the small integers code - 1, the product -s, 0, s or 2s: both
+// exact in fp16, one packed instruction each.
+KVQ_DEV uint32_t code_scale(uint32_t cw, uint32_t nb, uint32_t s2) {
+  const h2 c = __builtin_bit_cast(h2, cw) + __builtin_bit_cast(h2, nb);
+  return __builtin_bit_cast(uint32_t, c * __builtin_bit_cast(h2, s2));
+}
+
+// Token order of the score tiles.  An operand dword holds codes i and i + 8
+// of a word, so a thread's values pair tokens u and u + 8 of its 16, and
+// the PV k order follows: position 8 g' + 2 m + e of a k-step (lane group
+// g' supplies eight) holds token 16 (g' >> 1) + 4 (g' & 1) + m + 8 e.  QK
+// produces those scores in the lanes that supply them when row r of score
+// slab t is token slab_token(t, r).
+KVQ_DEV int slab_token(int t, int r) { return 32 * (t >> 1) + 8 * (t & 1) + (r & 7) + 16 * (r >> 3); }
 KVQ_DEV int pv_pos(int t) {
-  const int r = t & 31;
-  return (t & 32) + 8 * ((r & 15) >> 2) + (r & 3) + ((r & 16) ? 4 : 0);
+  const int u = t & 15, p = u & 7;
+  return (t & 32) + 8 * (2 * ((t >> 4) & 1) + (p >> 2)) + 2 * (p & 3) + (u >> 3);
+}
+
+// Orders a scheduling region of NR operand reads from LDS, each feeding two
+// MFMAs: DEPTH reads go first, then every read is issued two MFMAs ahead of
+// its turn, so the reads' latency hides under the matrix pipe.
+template <int NR, int DEPTH>
+KVQ_DEV void mfma_read_order() {
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+#pragma unroll
+  for (int i = 0; i < NR - DEPTH; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2 * DEPTH, 0);
 }
 
 template <int D, int VM>
@@ -127,20 +167,27 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
   constexpr int NKT = 64 * KW;       // key words per tile
   constexpr int NVT = D * 4;         // value words per tile (16 tokens each)
   constexpr bool HAD = VM != 0;
-  constexpr int KBUF = 64 * KP;
+  // window keys: rows 64 and 65 of a key buffer hold the channels'
+  // level-1 points (hi, lo), row 66 zeros
+  constexpr int KBUF = (KM == 0 ? 67 : 64) * KP;
+  constexpr int LBUF = 64 * KP;
   constexpr int VBUF = D * VP;
   constexpr int MBUF = NMU * 16 * VP;
   __shared__ __align__(16) _Float16 khi[2 * KBUF];
-  __shared__ __align__(16) _Float16 klo[2 * KBUF];
+  __shared__ __align__(16) _Float16 klo[2 * LBUF];
   __shared__ __align__(16) _Float16 vt[3 * VBUF];
   __shared__ __align__(16) _Float16 mut[3 * MBUF];
   // PSAC operand rows, 32 halves per token: a_hi, a_hi, a_lo, 0 (8 each);
   // 16-byte units swizzled by bits 2-3 of the token so the 16 rows an
   // operand read touches spread over the banks
   __shared__ __align__(16) _Float16 coef[R > 0 ? 2 * 64 * 32 : 8];
-  // parameters, two sets: tile t's in set t & 1, stored two tiles ahead
-  __shared__ __align__(16) uint32_t kpar[2][KM == 0 ? D : 64 * NG];   // window: per channel; else per token group
-  __shared__ __align__(16) uint32_t vpar[2][NG][64];                   // [group][token]
+  // parameters, two sets: tile t's in set t & 1, stored two tiles ahead.
+  // Window keys: per channel, as fp16 pairs in key-operand order, the s
+  // pairs in words 0 .. D/2 - 1, the z pairs after them; centroid keys:
+  // (s, z) per (token, group).  Values: per group, the s of tokens u and
+  // u + 8 of each 16 paired in words 0..31, the z pairs in words 32..63.
+  __shared__ __align__(16) uint32_t kpar[2][KM == 0 ? D : 64 * NG];
+  __shared__ __align__(16) uint32_t vpar[2][NG][64];
   __shared__ __align__(16) uint32_t vmod[2][VM == 2 ? 16 : 1];         // modality bytes of the tile
 
   const int rb = blockIdx.x % a.n_rb, split = blockIdx.x / a.n_rb;
@@ -151,6 +198,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
   const int g = lane >> 4, c16 = lane & 15;
   const int row0 = rb * kBM + wave * kNT * 16;
   const bool live = row0 < a.Lq;   // wave-uniform
+  const bool flip = (wave >> 2) & 1;  // the second wave of each SIMD
   const int n = a.n_tokens;
   const int n_tiles = (n + 63) / 64, n_full = n / 64;
   const int tile_begin = split * a.tiles_per_split;
@@ -161,6 +209,10 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
 
   CodeOr kor = {0x54005400u, 0x4C004C00u, 0x44004400u};
   asm volatile("" : "+v"(kor.b64), "+v"(kor.b16), "+v"(kor.b4));
+  // -(base + 1) in both halves for the three operand bases (64, 16, 4)
+  uint32_t nb65 = 0xD410D410u, nb17 = 0xCC40CC40u, nb5 = 0xC500C500u;
+  asm volatile("" : "+v"(nb65), "+v"(nb17), "+v"(nb5));
+  auto nbase = [&](int p) { return (p == 2 || p == 5) ? nb65 : ((p == 1 || p == 4 || p == 7) ? nb5 : nb17); };
 
   // ---- LDS set-up: value and row-sum buffers zero (the first PV step
   // multiplies a zero P by buffer 2), row 0 of every row-sum tile all ones
@@ -168,6 +220,8 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
     const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
     for (int e = tid; e < 3 * VBUF / 8; e += kThreads) reinterpret_cast<uint4*>(vt)[e] = z4;
     for (int e = tid; e < 3 * MBUF / 8; e += kThreads) reinterpret_cast<uint4*>(mut)[e] = z4;
+    if (KM == 0 && tid < 2 * D / 8)   // the zero row of both key buffers
+      reinterpret_cast<uint4*>(khi + (tid / (D / 8)) * KBUF + 66 * KP)[tid % (D / 8)] = z4;
     __syncthreads();
     if (tid < 3 * NMU * 64) {
       const int buf = tid / (NMU * 64), rest = tid % (NMU * 64), tile16 = rest / 64, t = rest % 64;
@@ -175,7 +229,10 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
     }
   }
 
-  // ---- queries (B operand), fp16 (exact from bf16), resident for the whole loop
+  // ---- queries (B operand), fp16 (exact from bf16), resident for the whole
+  // loop, in key-operand channel order: operand position 16 w + 2 p + e
+  // holds channel 16 w + p + 8 e (the two channels of one code dword), so
+  // lane group g of k-step ks takes channels c0 + {0, 8, 1, 9, 2, 10, 3, 11}
   h8 qreg[kNT][NKS];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
@@ -184,12 +241,15 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
     for (int ks = 0; ks < NKS; ++ks) {
       h8 v;
       if (row < a.Lq) {
-        const uint4 u = *reinterpret_cast<const uint4*>(
-            a.q + (((int64_t)b * a.Lq + row) * a.Hq + hq) * D + ks * 32 + 8 * g);
+        const uint16_t* qr = a.q + (((int64_t)b * a.Lq + row) * a.Hq + hq) * D + ks * 32 + 16 * (g >> 1) + 4 * (g & 1);
+        const uint2 u0 = *reinterpret_cast<const uint2*>(qr), u1 = *reinterpret_cast<const uint2*>(qr + 8);
         float x[8];
-        bf16x8_to_f32(u, x);
+        bf16x8_to_f32(make_uint4(u0.x, u1.x, u0.y, u1.y), x);   // channels c0, c0+1, c0+8, c0+9, ...
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = (_Float16)x[j];
+        for (int j = 0; j < 4; ++j) {
+          v[2 * j] = (_Float16)x[(j >> 1) * 4 + (j & 1)];
+          v[2 * j + 1] = (_Float16)x[(j >> 1) * 4 + 2 + (j & 1)];
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = (_Float16)0.0f;
@@ -259,30 +319,26 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
   }
 
   struct Pre {
-    uint32_t kcw, vcw, kp, vp, cf, cs, md;   // cf/cs: PSAC words (INT8: two codes, scale)
+    uint32_t kcw, vcw, cf, cs;   // cf/cs: PSAC words (INT8: two codes, scale)
     int ix;            // centroid index of token tk
     float cv[16];      // centroid channels 16 kw .. 16 kw + 15 of token tk
   };
-  // packed data of a tile into registers.  RAG (the ragged last tile):
-  // parameters and indices of rows past the length read as 0, so they
-  // dequantise to finite values; full tiles load unconditionally.
-  auto prefetch = [&](int tile, Pre& f, auto rag) {
+  struct Par {
+    uint32_t kp, vp, md;
+  };
+  // this thread's packed words of a tile: codes, centroid index, PSAC
+  // coefficients.  RAG (the ragged last tile): rows past the length read as
+  // 0, so they dequantise to finite values; full tiles load unconditionally.
+  auto load_codes = [&](int tile, Pre& f, auto rag) {
     constexpr bool RAG = decltype(rag)::value;
     const int t0 = tile * 64;
     const int64_t rowbase = bh * a.Tcap + t0;
-    const int pi = tid % (64 * NG);   // (token, group) parameter word
     f.kcw = has_k ? reinterpret_cast<const uint32_t*>(a.kcodes + rowbase * (D / 4))[tk * KW + kw] : 0u;
     f.vcw = has_v ? reinterpret_cast<const uint32_t*>(
                         a.vcodes + (bh * (a.Tcap / 64) + tile) * (int64_t)D * 16)[tid]
                   : 0u;
-    f.vp = a.vparams[rowbase * NG + pi];
-    if (RAG && t0 + pi / NG >= n) f.vp = 0u;
-    if (KM == 0) {
-      f.kp = (RAG && tile >= n_full) ? 0u : a.kparams[(bh * (a.Tcap / 64) + tile) * D + tid % D];
-    } else {
-      f.kp = a.kparams[rowbase * NG + pi];
+    if (KM != 0) {
       f.ix = has_k ? (int)a.kidx[rowbase + tk] : 0;
-      if (RAG && t0 + pi / NG >= n) f.kp = 0u;
       if (RAG && t0 + tk >= n) f.ix = 0;
     }
     f.cf = 0u;
@@ -302,6 +358,22 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
         f.cs = 0u;
       }
     }
+  };
+  // the tile's parameter words (value and key (z, s), modality bytes):
+  // threads 0 .. 255 cover every word and stage them in LDS
+  auto load_params = [&](int tile, Par& f, auto rag) {
+    constexpr bool RAG = decltype(rag)::value;
+    const int t0 = tile * 64;
+    const int64_t rowbase = bh * a.Tcap + t0;
+    const int pi = tid % (64 * NG);   // (token, group) parameter word
+    f.vp = a.vparams[rowbase * NG + pi];
+    if (RAG && t0 + pi / NG >= n) f.vp = 0u;
+    if (KM == 0) {
+      f.kp = (RAG && tile >= n_full) ? 0u : a.kparams[(bh * (a.Tcap / 64) + tile) * D + tid % D];
+    } else {
+      f.kp = a.kparams[rowbase * NG + pi];
+      if (RAG && t0 + pi / NG >= n) f.kp = 0u;
+    }
     f.md = 0u;
     if (VM == 2 && tid < 16)
       f.md = reinterpret_cast<const uint32_t*>(a.vmodal + (int64_t)b * a.Tcap + t0)[tid];
@@ -320,33 +392,33 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
       }
     }
   };
-  auto store_params = [&](int tile, const Pre& f) {
+  // (threads 0..255; beyond the words of a tile they repeat earlier ones)
+  auto store_params = [&](int tile, const Par& f) {
     const int ps = tile & 1;
-    vpar[ps][gm][tm] = f.vp;
-    if (KM == 0) kpar[ps][tid % D] = f.kp;
-    else kpar[ps][tid % (64 * NG)] = f.kp;
+    {
+      // token tm = 16 vq + 8 e + p: half e of pair word 8 vq + p
+      uint16_t* vw = reinterpret_cast<uint16_t*>(&vpar[ps][gm][0]);
+      const int hx = 2 * (8 * (tm >> 4) + (tm & 7)) + ((tm >> 3) & 1);
+      vw[hx] = (uint16_t)f.vp;
+      vw[64 + hx] = (uint16_t)(f.vp >> 16);
+    }
+    if (KM == 0) {
+      if (tid < D) {   // channel tid = 16 w + 8 e + p: operand position 16 w + 2 p + e
+        uint16_t* kw16 = reinterpret_cast<uint16_t*>(&kpar[ps][0]);
+        const int hx = 16 * (tid >> 4) + 2 * (tid & 7) + ((tid >> 3) & 1);
+        kw16[hx] = (uint16_t)f.kp;
+        kw16[D + hx] = (uint16_t)(f.kp >> 16);
+      }
+    } else {
+      kpar[ps][tid % (64 * NG)] = f.kp;
+    }
     if (VM == 2 && tid < 16) vmod[ps][tid] = f.md;
-  };
-
-  // Registers of the tile being dequantised (taken from Pre before the
-  // next tile's loads are issued into it).
-  struct Cur {
-    uint32_t kcw, vcw, cf, cs;
-    float cv[16];
-  };
-  auto take = [&](const Pre& f, Cur& c) {
-    c.kcw = f.kcw;
-    c.vcw = f.vcw;
-    c.cf = f.cf;
-    c.cs = f.cs;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) c.cv[i] = KM != 0 ? f.cv[i] : 0.0f;
   };
 
   // ---- dequantise tile `tile` into key buffer kb, value / row-sum buffer
   // vbuf, coefficient buffer kb.  RAG: the ragged last tile (window keys of
   // the unfinished window come from the tail; keys past the length are 0).
-  auto dequant = [&](int tile, const Cur& c, int kb, int vbuf, auto rag) {
+  auto dequant = [&](int tile, const Pre& c, int kb, int vbuf, auto rag) {
     constexpr bool RAG = decltype(rag)::value;
     const int ps = tile & 1;
     const int t0 = tile * 64;
@@ -373,25 +445,25 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
         *at(8 + j) = 0u;
       }
     }
-    // keys: token tk, channels 16 kw .. 16 kw + 15, as hi + lo
+    // keys: token tk, channels 16 kw + p and 16 kw + 8 + p in dword p
     if (has_k) {
-      float kv[16];
+      uint32_t hw[8], lw[8];
       const bool tail = RAG && KM == 0;   // the unfinished window
-      if (!tail) {
+      if (KM == 0 && !tail) {
+        // window keys: (code - 1) s, exact, one MFMA pass; the level-1 point
+        // z + s of each channel enters as a per-row bias
         uint32_t cw[8];
         code_word(c.kcw, kor, cw);
-        if (KM == 0) {
-          uint4 pw[4];
+        const uint4* sp4 = reinterpret_cast<const uint4*>(&kpar[ps][8 * kw]);
+        const uint4 s0 = sp4[0], s1 = sp4[1];
+        const uint32_t sp[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) pw[j] = *reinterpret_cast<const uint4*>(&kpar[ps][16 * kw + 4 * j]);
-          const uint32_t pv[16] = {pw[0].x, pw[0].y, pw[0].z, pw[0].w, pw[1].x, pw[1].y, pw[1].z, pw[1].w,
-                                   pw[2].x, pw[2].y, pw[2].z, pw[2].w, pw[3].x, pw[3].y, pw[3].z, pw[3].w};
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float s = f16_bits_to_f32(pv[i]), z = f16_bits_to_f32(pv[i] >> 16);
-            kv[i] = fma_code(cw[i & 7], i >= 8, s, __builtin_fmaf(-code_base(i & 7), s, z));
-          }
-        } else {
+        for (int p = 0; p < 8; ++p) hw[p] = code_scale(cw[p], nbase(p), sp[p]);
+      } else {
+        float kv[16];
+        if (!tail) {
+          uint32_t cw[8];
+          code_word(c.kcw, kor, cw);
           const uint32_t pw = kpar[ps][tk * NG + kw / 2];
           const float s = f16_bits_to_f32(pw), z = f16_bits_to_f32(pw >> 16);
           const float z16 = __builtin_fmaf(-16.0f, s, z), z4 = __builtin_fmaf(-4.0f, s, z),
@@ -403,83 +475,79 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
             // centroid + residual (the residual rounded to fp32 first)
             kv[i] = c.cv[i] + fma_code(cw[p], i >= 8, s, zb);
           }
+        } else {
+          const uint16_t* kt = a.ktail + (bh * 64 + tk) * D + 16 * kw;
+          bf16x8_to_f32(*reinterpret_cast<const uint4*>(kt), kv);
+          bf16x8_to_f32(*reinterpret_cast<const uint4*>(kt + 8), kv + 8);
         }
-      } else {
-        const uint16_t* kt = a.ktail + (bh * 64 + tk) * D + 16 * kw;
-        bf16x8_to_f32(*reinterpret_cast<const uint4*>(kt), kv);
-        bf16x8_to_f32(*reinterpret_cast<const uint4*>(kt + 8), kv + 8);
-      }
-      if (RAG && t0 + tk >= n) {
+        if (RAG && t0 + tk >= n) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) kv[i] = 0.0f;
-      }
-      uint32_t hw[8], lw[8];
+          for (int i = 0; i < 16; ++i) kv[i] = 0.0f;
+        }
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        hw[m] = pk_rne(kv[2 * m], kv[2 * m + 1]);
-        const h2 hh = __builtin_bit_cast(h2, hw[m]);
-        lw[m] = pk_rne(kv[2 * m] - (float)hh[0], kv[2 * m + 1] - (float)hh[1]);
+        for (int p = 0; p < 8; ++p) {
+          hw[p] = pk_rne(kv[p], kv[p + 8]);
+          lw[p] = lo_pair(hw[p], kv[p], kv[p + 8]);
+        }
       }
       // 16-byte units 2 kw, 2 kw + 1 of row tk, swapped in odd rows
-      const int o0 = kb * KBUF + tk * KP + 8 * ((2 * kw) ^ (tk & 1));
-      const int o1 = kb * KBUF + tk * KP + 8 * ((2 * kw + 1) ^ (tk & 1));
-      *reinterpret_cast<uint4*>(&khi[o0]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      *reinterpret_cast<uint4*>(&khi[o1]) = make_uint4(hw[4], hw[5], hw[6], hw[7]);
-      *reinterpret_cast<uint4*>(&klo[o0]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-      *reinterpret_cast<uint4*>(&klo[o1]) = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+      const int o0 = tk * KP + 8 * ((2 * kw) ^ (tk & 1));
+      const int o1 = tk * KP + 8 * ((2 * kw + 1) ^ (tk & 1));
+      *reinterpret_cast<uint4*>(&khi[kb * KBUF + o0]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *reinterpret_cast<uint4*>(&khi[kb * KBUF + o1]) = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+      if (KM != 0 || tail) {
+        *reinterpret_cast<uint4*>(&klo[kb * LBUF + o0]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        *reinterpret_cast<uint4*>(&klo[kb * LBUF + o1]) = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+      }
     }
-    // values: channel vc, tokens 16 vq .. 16 vq + 15, centred on level 1,
-    // (code - 1) s = (base + code) s - (base + 1) s, exact in fp32 and fp16,
-    // written in operand order: position 32 kk + 8 g' + j holds token
-    // 32 kk + 4 g' + j (j < 4) or 32 kk + 16 + 4 g' + j - 4 (j >= 4)
+    // window keys: each channel's level-1 point z + s as fp16 hi (row 64)
+    // and lo (row 65) of the key buffer, at the channel's operand position
+    if (KM == 0 && !RAG && tid < D) {
+      const uint16_t* kw16 = reinterpret_cast<const uint16_t*>(&kpar[ps][0]);
+      const int hx = 16 * (tid >> 4) + 2 * (tid & 7) + ((tid >> 3) & 1);
+      const float mu = f16_bits_to_f32(kw16[D + hx]) + f16_bits_to_f32(kw16[hx]);
+      const _Float16 mh = (_Float16)opaque(mu);
+      khi[kb * KBUF + 64 * KP + hx] = mh;
+      khi[kb * KBUF + 65 * KP + hx] = (_Float16)(mu - (float)mh);
+    }
+    // values: channel vc, tokens 16 vq + p and 16 vq + 8 + p in dword p,
+    // (code - 1) s (exact); with the PV token order the eight dwords are the
+    // two 16-byte units 2 (vq & 1) and 2 (vq & 1) + 1 of k-step vq / 2
+    // (swapped in pairs of rows)
     if (has_v) {
       uint32_t cw[8];
       code_word(c.vcw, kor, cw);
-      const uint4* pr = reinterpret_cast<const uint4*>(&vpar[ps][vc / kGroup][16 * vq]);
-      const uint4 p4[4] = {pr[0], pr[1], pr[2], pr[3]};
-      const uint32_t pv[16] = {p4[0].x, p4[0].y, p4[0].z, p4[0].w, p4[1].x, p4[1].y, p4[1].z, p4[1].w,
-                               p4[2].x, p4[2].y, p4[2].z, p4[2].w, p4[3].x, p4[3].y, p4[3].z, p4[3].w};
-      float vv[16];   // token 16 vq + u
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int p = u & 7;
-        const float s = f16_bits_to_f32(pv[u]);
-        vv[u] = fma_code(cw[p], u >= 8, s, -(code_base(p) + 1.0f) * s);
-      }
+      const uint4* sp4 = reinterpret_cast<const uint4*>(&vpar[ps][vc / kGroup][8 * vq]);
+      const uint4 s0 = sp4[0], s1 = sp4[1];
+      const uint32_t sp[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
       uint32_t pk[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pk[j] = pk_rne(vv[2 * j], vv[2 * j + 1]);
+      for (int p = 0; p < 8; ++p) pk[p] = code_scale(cw[p], nbase(p), sp[p]);
       if (VM == 2) {
         // sign of (token, channel vc): bit m(t) of vsgn; negate those halves
         const uint32_t* mw = &vmod[ps][4 * vq];
-        uint32_t neg = 0u;   // bit u: token 16 vq + u negated
 #pragma unroll
         for (int w4 = 0; w4 < 4; ++w4) {
           const uint32_t mb = mw[w4];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
+            const int u = 4 * w4 + k;   // token 16 vq + u
             const uint32_t m = min((mb >> (8 * k)) & 0xFFu, (uint32_t)(M - 1));
-            neg |= ((vsgn >> m) & 1u) << (4 * w4 + k);
+            pk[u & 7] ^= ((vsgn >> m) & 1u) << (15 + 16 * (u >> 3));
           }
         }
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          pk[j] ^= (((neg >> (2 * j)) & 1u) << 15) | (((neg >> (2 * j + 1)) & 1u) << 31);
       }
-      // tokens 16 vq + 4 gg + j: k-step vq / 2, positions 8 gg + 4 (vq & 1) + j
-      // (16-byte units swapped in pairs when bit 1 of the row is set)
-      _Float16* dst = &vt[vbuf * VBUF + vc * VP + 32 * (vq >> 1) + 4 * (vq & 1)];
-      const int vs = (vc >> 1) & 1;
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg)
-        *reinterpret_cast<uint2*>(dst + 8 * (gg ^ vs)) = make_uint2(pk[2 * gg], pk[2 * gg + 1]);
+      _Float16* dst = &vt[vbuf * VBUF + vc * VP + 32 * (vq >> 1)];
+      const int vs = (vc >> 1) & 1, u0 = 2 * (vq & 1);
+      *reinterpret_cast<uint4*>(dst + 8 * (u0 ^ vs)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      *reinterpret_cast<uint4*>(dst + 8 * ((u0 + 1) ^ vs)) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
     }
     // row sums: level 1, z + s, of (token tm, group gm) as fp16 hi and lo,
     // in the rows of the token's modality (zero in the others)
     {
-      const uint32_t pw = vpar[ps][gm][tm];
-      const float s = f16_bits_to_f32(pw), z = f16_bits_to_f32(pw >> 16);
-      const float mu = z + s;
+      const uint16_t* vw = reinterpret_cast<const uint16_t*>(&vpar[ps][gm][0]);
+      const int hx = 2 * (8 * (tm >> 4) + (tm & 7)) + ((tm >> 3) & 1);
+      const float mu = f16_bits_to_f32(vw[64 + hx]) + f16_bits_to_f32(vw[hx]);
       const _Float16 mh = (_Float16)opaque(mu);
       const _Float16 ml = (_Float16)(mu - (float)mh);
       int mt = 0;
@@ -498,36 +566,59 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
     }
   };
 
-  // ---- S^T = Khat Q^T for tokens 32 half .. 32 half + 31 of key buffer kb
-  // (hi and lo, PSAC k-step first); s[nt][t] holds token slab 2 half + t
-  auto qk = [&](int kb, int half, f4 (&s)[kNT][2]) {
+  // ---- S^T = Khat Q^T for the 64 tokens of key buffer kb, row r of slab
+  // t holding token slab_token(t, r): PSAC k-step first, then hi (and lo,
+  // TWO) of every k-step.  One pass (window keys): cst gets the level-1
+  // points' products, rows 4g and 4g + 1 (hi, lo) of every lane group.
+  auto qk = [&](int kb, f4 (&s)[kNT][4], auto two, f4 (&cst)[kNT]) {
+    constexpr bool TWO = decltype(two)::value;
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
+    for (int nt = 0; nt < kNT; ++nt) {
+      cst[nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int t = 0; t < 2; ++t) s[nt][t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int t = 0; t < 4; ++t) s[nt][t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
     const _Float16* kh = khi + kb * KBUF;
-    const _Float16* kl = klo + kb * KBUF;
+    const _Float16* kl = klo + kb * LBUF;
+    if (R > 0) {
+      // row slab_token(t, c16) of the coefficient tile (k 0..23)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int ts = 2 * half + t;
-      if (R > 0) {
-        // PSAC first: row ts*16 + c16 of the coefficient tile (k 0..23)
-        const int cr = ts * 16 + c16;
+      for (int t = 0; t < 4; ++t) {
+        const int cr = slab_token(t, c16);
         const h8 ca = *reinterpret_cast<const h8*>(&coef[kb * 64 * 32 + cr * 32 + 8 * (g ^ ((cr >> 2) & 3))]);
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt)
           s[nt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca, qp[nt], s[nt][t], 0, 0, 0);
       }
+    }
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int off = (ts * 16 + c16) * KP + ks * 32 + 8 * (g ^ (c16 & 1));
-        const h8 ka = *reinterpret_cast<const h8*>(&kh[off]);
-        const h8 kl2 = *reinterpret_cast<const h8*>(&kl[off]);
+    for (int ks = 0; ks < NKS; ++ks) {
+      h8 ka[4], kl2[4];
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          s[nt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qreg[nt][ks], s[nt][t], 0, 0, 0);
-          s[nt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kl2, qreg[nt][ks], s[nt][t], 0, 0, 0);
-        }
+      for (int t = 0; t < 4; ++t) {
+        // (a token's parity is c16's, which picks the unit swap)
+        const int off = slab_token(t, c16) * KP + ks * 32 + 8 * (g ^ (c16 & 1));
+        ka[t] = *reinterpret_cast<const h8*>(&kh[off]);
+        if (TWO) kl2[t] = *reinterpret_cast<const h8*>(&kl[off]);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+          s[nt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[t], qreg[nt][ks], s[nt][t], 0, 0, 0);
+      if (TWO) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt)
+            s[nt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kl2[t], qreg[nt][ks], s[nt][t], 0, 0, 0);
+      } else if (KM == 0) {
+        // A rows c16 = 4i (hi), 4i + 1 (lo) of the level-1 points, others zero
+        const int mr = 64 + ((c16 & 3) < 2 ? (c16 & 3) : 2);
+        const h8 am = *reinterpret_cast<const h8*>(&kh[mr * KP + ks * 32 + 8 * g]);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+          cst[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, qreg[nt][ks], cst[nt], 0, 0, 0);
       }
     }
   };
@@ -556,23 +647,28 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
     }
   };
 
-  // ---- online softmax (base 2) of one half tile's scores into P (fp16);
-  // lane owns row nt*16 + c16, tokens 32 half + 16 t + 4g + i.  row_max
-  // returns whether some row's reference maximum must move (then `grow`).
-  auto row_max = [&](const f4 (&s)[kNT][2], float (&lm)[kNT]) {
+  // ---- online softmax (base 2) of a tile's scores into P (fp16); lane
+  // owns row nt*16 + c16, scores s[nt][t][i] of token slab_token(t, 4g + i)
+  // plus the row's bias (window keys: the level-1 points' product).
+  // row_max returns whether some row's reference maximum must move (then
+  // `grow`).
+  auto row_max = [&](const f4 (&s)[kNT][4], const float (&bias)[kNT], float (&lm)[kNT]) {
     bool gr = false;
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
       float m = -__builtin_inff();
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 4; ++t)
         m = fmaxf(fmaxf(m, fmaxf(s[nt][t][0], s[nt][t][1])), fmaxf(s[nt][t][2], s[nt][t][3]));
-      lm[nt] = m;
-      gr |= m > thr[nt];
+      lm[nt] = m + bias[nt];
+      gr |= lm[nt] > thr[nt];
     }
     return gr;
   };
   auto grow = [&](const float (&lm)[kNT]) {
+    // a real branch: without this the compiler may run the rescale of
+    // every accumulator unconditionally (by an alpha of 1)
+    asm volatile("");
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
       float m = lm[nt];
@@ -588,132 +684,146 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
       for (int dt = 0; dt < NDT; ++dt) o[nt][dt] *= alpha;
     }
   };
-  // P of a half tile: the B operand of PV k-step `half` (slabs 2 half, 2 half + 1)
-  auto probs = [&](const f4 (&s)[kNT][2], h8 (&pb)[kNT]) {
+  // P: the B operands of the two PV k-steps; dword m of k-step kk pairs the
+  // m-th scores of slabs 2 kk and 2 kk + 1 (tokens 8 apart)
+  auto probs = [&](const f4 (&s)[kNT][4], const float (&bias)[kNT], h8 (&pb)[kNT][2]) {
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
-      uint32_t pw[4];
+      const float off = __builtin_fmaf(bias[nt], a.scale_log2, -m_run[nt]);
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int kk = 0; kk < 2; ++kk) {
+        uint32_t pw[4];
 #pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nt][t][i], a.scale_log2, -m_run[nt]));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nt][t][i + 1], a.scale_log2, -m_run[nt]));
-          pw[t * 2 + i / 2] = pk_rne(p0, p1);
+        for (int m = 0; m < 4; ++m) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nt][2 * kk][m], a.scale_log2, off));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nt][2 * kk + 1][m], a.scale_log2, off));
+          pw[m] = pk_rne(p0, p1);
         }
-      pb[nt] = as_h8(pw[0], pw[1], pw[2], pw[3]);
+        pb[nt][kk] = as_h8(pw[0], pw[1], pw[2], pw[3]);
+      }
     }
   };
-  // masks the scores of tokens at or past the length (ragged last tile)
-  auto mask = [&](int t0, int half, f4 (&s)[kNT][2]) {
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (t0 + 32 * half + 16 * t + 4 * g + i >= n) s[nt][t][i] = -__builtin_inff();
-  };
-  // QK and P of tile buffer kb: the second half's MFMAs run while the first
-  // half's probabilities are formed; a rare move of the reference maximum
-  // in the second half re-forms the first half's.
-  auto qk_softmax = [&](int kb, h8 (&pb)[kNT][2], int t0, auto rag) {
+  // RAG: the scores of tokens at or past the length are masked
+  auto softmax = [&](f4 (&s)[kNT][4], const float (&bias)[kNT], h8 (&pb)[kNT][2], int t0, auto rag) {
     constexpr bool RAG = decltype(rag)::value;
-    f4 sa[kNT][2], sb[kNT][2];
-    float lm[kNT];
-    qk(kb, 0, sa);
-    if (RAG) mask(t0, 0, sa);
-    if (__any(row_max(sa, lm))) grow(lm);
-    h8 pa[kNT];
-    qk(kb, 1, sb);
-    probs(sa, pa);
-    if (RAG) mask(t0, 1, sb);
-    if (__any(row_max(sb, lm))) {
-      grow(lm);
-      probs(sa, pa);
-    }
-    h8 pc[kNT];
-    probs(sb, pc);
+    if (RAG) {
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-      pb[nt][0] = pa[nt];
-      pb[nt][1] = pc[nt];
+      for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (t0 + slab_token(t, 4 * g + i) >= n) s[nt][t][i] = -__builtin_inff();
     }
+    float lm[kNT];
+    if (__builtin_expect(__any(row_max(s, bias, lm)), 0)) grow(lm);
+    probs(s, bias, pb);
   };
 
-  // P of the previous tile (zero before the first: its PV step adds nothing)
-  h8 pprev[kNT][2];
+  // P of the previous tile, S of the current one
+  h8 pb[kNT][2];
+  f4 sc[kNT][4], cst[kNT];
+  float bias[kNT] = {};
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pprev[nt][kk][j] = (_Float16)0.0f;
+      for (int j = 0; j < 8; ++j) pb[nt][kk][j] = (_Float16)0.0f;
 
-  Pre pre;
-  Cur cur;
+  // ---- ping-pong over the SIMDs.  Waves w and w + 4 share a SIMD; each
+  // alternates a matrix phase (QK of tile k, PV of tile k - 1) with a
+  // vector phase (softmax of tile k, its share of the dequantisation of a
+  // later tile, the next loads), one barrier per phase.  The second group
+  // (waves 4..7) runs one phase behind the first, so in every phase one
+  // wave of each SIMD feeds the matrix pipe while the other keeps the
+  // vector pipe busy.  Tile k + 1 is dequantised by the first group in its
+  // vector phase k and by the second in its vector phase k - 1, both
+  // before either group's matrix phase k + 1; with the phase offset a key
+  // buffer is rewritten two phases after its last read (two buffers) and
+  // a value buffer four (three buffers).  The first group (threads
+  // 0..255) stages the parameter words, two tiles ahead.  Packed codes are
+  // requested a matrix phase before their vector phase, which first asks
+  // for the centroid rows they index and forms P while those arrive.  (A wave whose rows
+  // are all past the end only dequantises and keeps the barriers.)
+  auto phase = [&]() {
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // cur: the packed words (and centroid rows) of the tile this wave
+  // dequantises next, requested a matrix phase ahead; par: parameter
+  // words, stored the phase pair after they arrive.  The loop's loads are
+  // unconditional (a tile index past the end reads the last full tile
+  // again), so no loaded register is copied at the loop's end, which would
+  // wait for the load.
+  Pre cur;
+  Par par;
   const int nfull = full_end - tile_begin;
   if (nfull > 0) {
-    // ---- prologue: tile 0 of the split dequantised, tile 1's parameters stored
-    prefetch(tile_begin, pre, std::false_type{});
-    prefetch_cent(pre);
-    store_params(tile_begin, pre);
+    const int last = full_end - 1;
+    load_codes(tile_begin, cur, std::false_type{});
+    if (!flip) load_params(tile_begin, par, std::false_type{});
+    prefetch_cent(cur);
+    if (!flip) {
+      store_params(tile_begin, par);
+      if (nfull > 1) {
+        load_params(tile_begin + 1, par, std::false_type{});
+        store_params(tile_begin + 1, par);
+      }
+    }
     __syncthreads();
-    take(pre, cur);
-    if (nfull > 1) prefetch(tile_begin + 1, pre, std::false_type{});
     dequant(tile_begin, cur, 0, 0, std::false_type{});
-    if (nfull > 1) {
-      prefetch_cent(pre);
-      store_params(tile_begin + 1, pre);
+    load_codes(min(tile_begin + 1, last), cur, std::false_type{});
+    load_params(min(tile_begin + 2, last), par, std::false_type{});
+    if (flip) {   // the second group's vector phase -1: its share of tile 1
+      phase();
+      prefetch_cent(cur);
+      if (nfull > 1) dequant(tile_begin + 1, cur, 1, 1, std::false_type{});
+      load_codes(min(tile_begin + 2, last), cur, std::false_type{});
     }
+    for (int k = 0; k < nfull; ++k) {
+      const int dq = k + 1 + (flip ? 1 : 0);   // the tile this wave dequantises next
+      phase();   // ---- matrix phase k
+      if (live) {
+        // (at k = 0, P is zero and value buffer 2 still holds its zeros)
+        __builtin_amdgcn_s_setprio(1);
+        qk(k & 1, sc, std::integral_constant<bool, KM != 0>{}, cst);
+        pv((k + 2) % 3, pb);
+        mfma_read_order<(R > 0 ? 4 : 0) + (KM != 0 ? 8 : 5) * NKS + 2 * (NDT + NMU), 6>();
+        __builtin_amdgcn_s_setprio(0);
+        if (KM == 0) {
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt) bias[nt] = cst[nt][0] + cst[nt][1];
+        }
+      }
+      phase();   // ---- vector phase k
+      prefetch_cent(cur);   // its index arrived during the matrix phase
+      if (live) softmax(sc, bias, pb, 0, std::false_type{});
+      if (dq < nfull) dequant(tile_begin + dq, cur, dq & 1, dq % 3, std::false_type{});
+      if (!flip && k + 2 < nfull) store_params(tile_begin + k + 2, par);
+      load_codes(min(tile_begin + dq + 1, last), cur, std::false_type{});
+      load_params(min(tile_begin + k + 3, last), par, std::false_type{});
+    }
+    if (!flip) phase();   // meets the second group's last vector phase
+    // PV of the last full tile
+    if (live) pv((nfull - 1) % 3, pb);
   }
-
-  // ---- one pipelined step: PV of tile j - 1 with the dequantisation of
-  // tile j + 1, then QK and P of tile j.  DQ: tile j + 1 exists; PF: tile
-  // j + 2 exists (its packed data is requested after the dequantisation).
-  auto step = [&](int j, auto dq, auto pf) {
-    constexpr bool DQ = decltype(dq)::value, PF = decltype(pf)::value;
-    const int k = j - tile_begin;
-    __syncthreads();
-    if (DQ) take(pre, cur);
-    // one straight-line block per kind of wave, so that the PV MFMAs and
-    // the dequantisation can be interleaved
-    if (live) {
-      pv((k + 2) % 3, pprev);
-      if (DQ) dequant(j + 1, cur, (k + 1) & 1, (k + 1) % 3, std::false_type{});
-    } else {
-      if (DQ) dequant(j + 1, cur, (k + 1) & 1, (k + 1) % 3, std::false_type{});
-    }
-    if (PF) prefetch(j + 2, pre, std::false_type{});
-    if (live) qk_softmax(k & 1, pprev, j * 64, std::false_type{});
-    if (PF) {
-      prefetch_cent(pre);
-      store_params(j + 2, pre);
-    }
-  };
-  {
-    int j = tile_begin;
-    for (; j + 2 < full_end; ++j) step(j, std::true_type{}, std::true_type{});
-    if (j + 1 < full_end) step(j++, std::true_type{}, std::false_type{});
-    if (j < full_end) step(j++, std::false_type{}, std::false_type{});
-  }
-  // drain: PV of the last full tile
-  if (nfull > 0 && live) pv((nfull - 1) % 3, pprev);
 
   // ---- the ragged last tile, unpipelined
   if (has_ragged) {
     const int tile = tile_end - 1;
     __syncthreads();   // every buffer is free
-    prefetch(tile, pre, std::true_type{});
-    prefetch_cent(pre);
-    store_params(tile, pre);
+    load_codes(tile, cur, std::true_type{});
+    if (!flip) load_params(tile, par, std::true_type{});
+    prefetch_cent(cur);
+    if (!flip) store_params(tile, par);
     __syncthreads();
-    take(pre, cur);
     dequant(tile, cur, 0, 0, std::true_type{});
     __syncthreads();
     if (live) {
-      h8 pb[kNT][2];
-      qk_softmax(0, pb, tile * 64, std::true_type{});
+      const float zero[kNT] = {};
+      qk(0, sc, std::true_type{}, cst);
+      softmax(sc, zero, pb, tile * 64, std::true_type{});
       pv(0, pb);
     }
   }
