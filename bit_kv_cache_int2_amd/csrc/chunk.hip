@@ -181,6 +181,13 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
   // 16-byte units swizzled by bits 2-3 of the token so the 16 rows an
   // operand read touches spread over the banks
   __shared__ __align__(16) _Float16 coef[R > 0 ? 2 * 64 * 32 : 8];
+  // PSAC: each wave's q'_hi (halves 0..7) and q'_lo (8..15) per query row,
+  // the B operand of the PSAC k-step, kept here rather than in registers
+  // where the LDS has room for it
+  constexpr int kLdsBytes = 2 * (2 * KBUF + 2 * LBUF + 3 * VBUF + 3 * MBUF + (R > 0 ? 2 * 64 * 32 : 8)) +
+                            4 * (2 * (KM == 0 ? D : 64 * NG) + 2 * NG * 64 + 2 * (VM == 2 ? 16 : 1));
+  constexpr bool QPL = R > 0 && kLdsBytes + 2 * kWaves * kNT * 16 * 16 <= 160 * 1024;
+  __shared__ __align__(16) _Float16 qpl[QPL ? kWaves * kNT * 16 * 16 : 8];
   // parameters, two sets: tile t's in set t & 1, stored two tiles ahead.
   // Window keys: per channel, as fp16 pairs in key-operand order, the s
   // pairs in words 0 .. D/2 - 1, the z pairs after them; centroid keys:
@@ -258,16 +265,18 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
     }
   }
   // ---- PSAC: q' = U^T q, the B operand of one more 16x16x32 k-step: lanes
-  // g = 0, 1, 2 supply q'_hi, q'_lo, q'_hi of their row (k 0..23), g = 3 zero
+  // g = 0, 1, 2 supply q'_hi, q'_lo, q'_hi of their row (k 0..23); g = 3
+  // supplies q'_hi again, against the coefficient tile's zeros (k 24..31)
   static_assert(R == 0 || R == 8, "PSAC rank 8 fills k 0..23 of one k-step");
-  h8 qp[kNT];
+  h8 qpr[kNT];   // (without room in the LDS)
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
+    if (R > 0 && (g < 2 || !QPL)) {
+      h8 qv;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) qp[nt][j] = (_Float16)0.0f;
-    if (R > 0) {
+      for (int j = 0; j < 8; ++j) qv[j] = (_Float16)0.0f;
       const int row = row0 + nt * 16 + c16;
-      if (g < 3 && row < a.Lq) {
+      if (row < a.Lq) {
         const uint16_t* qr = a.q + (((int64_t)b * a.Lq + row) * a.Hq + hq) * D;
         const float* U = a.basis + bh * D * (R > 0 ? R : 1);
         float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
@@ -279,9 +288,11 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const _Float16 hi = (_Float16)opaque(acc[j]);
-          qp[nt][j] = (g == 1) ? (_Float16)(acc[j] - (float)hi) : hi;
+          qv[j] = (g == 1) ? (_Float16)(acc[j] - (float)hi) : hi;
         }
       }
+      if (QPL) *reinterpret_cast<h8*>(&qpl[((wave * kNT + nt) * 16 + c16) * 16 + 8 * g]) = qv;
+      else qpr[nt] = qv;
     }
   }
 
@@ -418,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
   // ---- dequantise tile `tile` into key buffer kb, value / row-sum buffer
   // vbuf, coefficient buffer kb.  RAG: the ragged last tile (window keys of
   // the unfinished window come from the tail; keys past the length are 0).
-  auto dequant = [&](int tile, const Pre& c, int kb, int vbuf, auto rag) {
+  auto dequant_v = [&](int tile, const Pre& c, int kb, int vbuf, auto rag) {
     constexpr bool RAG = decltype(rag)::value;
     const int ps = tile & 1;
     const int t0 = tile * 64;
@@ -445,6 +456,65 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
         *at(8 + j) = 0u;
       }
     }
+    // values: channel vc, tokens 16 vq + p and 16 vq + 8 + p in dword p,
+    // (code - 1) s (exact); with the PV token order the eight dwords are the
+    // two 16-byte units 2 (vq & 1) and 2 (vq & 1) + 1 of k-step vq / 2
+    // (swapped in pairs of rows)
+    if (has_v) {
+      uint32_t cw[8];
+      code_word(c.vcw, kor, cw);
+      const uint4* sp4 = reinterpret_cast<const uint4*>(&vpar[ps][vc / kGroup][8 * vq]);
+      const uint4 s0 = sp4[0], s1 = sp4[1];
+      const uint32_t sp[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      uint32_t pk[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) pk[p] = code_scale(cw[p], nbase(p), sp[p]);
+      if (VM == 2) {
+        // sign of (token, channel vc): bit m(t) of vsgn; negate those halves
+        const uint32_t* mw = &vmod[ps][4 * vq];
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+          const uint32_t mb = mw[w4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int u = 4 * w4 + k;   // token 16 vq + u
+            const uint32_t m = min((mb >> (8 * k)) & 0xFFu, (uint32_t)(M - 1));
+            pk[u & 7] ^= ((vsgn >> m) & 1u) << (15 + 16 * (u >> 3));
+          }
+        }
+      }
+      _Float16* dst = &vt[vbuf * VBUF + vc * VP + 32 * (vq >> 1)];
+      const int vs = (vc >> 1) & 1, u0 = 2 * (vq & 1);
+      *reinterpret_cast<uint4*>(dst + 8 * (u0 ^ vs)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      *reinterpret_cast<uint4*>(dst + 8 * ((u0 + 1) ^ vs)) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+    }
+    // row sums: level 1, z + s, of (token tm, group gm) as fp16 hi and lo,
+    // in the rows of the token's modality (zero in the others)
+    {
+      const uint16_t* vw = reinterpret_cast<const uint16_t*>(&vpar[ps][gm][0]);
+      const int hx = 2 * (8 * (tm >> 4) + (tm & 7)) + ((tm >> 3) & 1);
+      const float mu = f16_bits_to_f32(vw[64 + hx]) + f16_bits_to_f32(vw[hx]);
+      const _Float16 mh = (_Float16)opaque(mu);
+      const _Float16 ml = (_Float16)(mu - (float)mh);
+      int mt = 0;
+      if (VM == 2) mt = min((int)((vmod[ps][tm >> 2] >> (8 * (tm & 3))) & 0xFFu), M - 1);
+      const int pos = pv_pos(tm);
+      constexpr int MM = Shape<D, VM>::M;
+      for (int m = 0; m < (VM == 2 ? M : 1); ++m) {
+        const int rh = 1 + m * NG + gm;
+        const int rl = 1 + MM * NG + m * NG + gm;
+        const bool mine = (m == mt);
+        const int ph = (pos & ~24) | ((((pos >> 3) & 3) ^ ((rh >> 1) & 1)) << 3);
+        const int pl = (pos & ~24) | ((((pos >> 3) & 3) ^ ((rl >> 1) & 1)) << 3);
+        mut[vbuf * MBUF + rh * VP + ph] = mine ? mh : (_Float16)0.0f;
+        mut[vbuf * MBUF + rl * VP + pl] = mine ? ml : (_Float16)0.0f;
+      }
+    }
+  };
+  auto dequant_k = [&](int tile, const Pre& c, int kb, auto rag) {
+    constexpr bool RAG = decltype(rag)::value;
+    const int ps = tile & 1;
+    const int t0 = tile * 64;
     // keys: token tk, channels 16 kw + p and 16 kw + 8 + p in dword p
     if (has_k) {
       uint32_t hw[8], lw[8];
@@ -510,60 +580,11 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
       khi[kb * KBUF + 64 * KP + hx] = mh;
       khi[kb * KBUF + 65 * KP + hx] = (_Float16)(mu - (float)mh);
     }
-    // values: channel vc, tokens 16 vq + p and 16 vq + 8 + p in dword p,
-    // (code - 1) s (exact); with the PV token order the eight dwords are the
-    // two 16-byte units 2 (vq & 1) and 2 (vq & 1) + 1 of k-step vq / 2
-    // (swapped in pairs of rows)
-    if (has_v) {
-      uint32_t cw[8];
-      code_word(c.vcw, kor, cw);
-      const uint4* sp4 = reinterpret_cast<const uint4*>(&vpar[ps][vc / kGroup][8 * vq]);
-      const uint4 s0 = sp4[0], s1 = sp4[1];
-      const uint32_t sp[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-      uint32_t pk[8];
-#pragma unroll
-      for (int p = 0; p < 8; ++p) pk[p] = code_scale(cw[p], nbase(p), sp[p]);
-      if (VM == 2) {
-        // sign of (token, channel vc): bit m(t) of vsgn; negate those halves
-        const uint32_t* mw = &vmod[ps][4 * vq];
-#pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4) {
-          const uint32_t mb = mw[w4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int u = 4 * w4 + k;   // token 16 vq + u
-            const uint32_t m = min((mb >> (8 * k)) & 0xFFu, (uint32_t)(M - 1));
-            pk[u & 7] ^= ((vsgn >> m) & 1u) << (15 + 16 * (u >> 3));
-          }
-        }
-      }
-      _Float16* dst = &vt[vbuf * VBUF + vc * VP + 32 * (vq >> 1)];
-      const int vs = (vc >> 1) & 1, u0 = 2 * (vq & 1);
-      *reinterpret_cast<uint4*>(dst + 8 * (u0 ^ vs)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      *reinterpret_cast<uint4*>(dst + 8 * ((u0 + 1) ^ vs)) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-    }
-    // row sums: level 1, z + s, of (token tm, group gm) as fp16 hi and lo,
-    // in the rows of the token's modality (zero in the others)
-    {
-      const uint16_t* vw = reinterpret_cast<const uint16_t*>(&vpar[ps][gm][0]);
-      const int hx = 2 * (8 * (tm >> 4) + (tm & 7)) + ((tm >> 3) & 1);
-      const float mu = f16_bits_to_f32(vw[64 + hx]) + f16_bits_to_f32(vw[hx]);
-      const _Float16 mh = (_Float16)opaque(mu);
-      const _Float16 ml = (_Float16)(mu - (float)mh);
-      int mt = 0;
-      if (VM == 2) mt = min((int)((vmod[ps][tm >> 2] >> (8 * (tm & 3))) & 0xFFu), M - 1);
-      const int pos = pv_pos(tm);
-      constexpr int MM = Shape<D, VM>::M;
-      for (int m = 0; m < (VM == 2 ? M : 1); ++m) {
-        const int rh = 1 + m * NG + gm;
-        const int rl = 1 + MM * NG + m * NG + gm;
-        const bool mine = (m == mt);
-        const int ph = (pos & ~24) | ((((pos >> 3) & 3) ^ ((rh >> 1) & 1)) << 3);
-        const int pl = (pos & ~24) | ((((pos >> 3) & 3) ^ ((rl >> 1) & 1)) << 3);
-        mut[vbuf * MBUF + rh * VP + ph] = mine ? mh : (_Float16)0.0f;
-        mut[vbuf * MBUF + rl * VP + pl] = mine ? ml : (_Float16)0.0f;
-      }
-    }
+  };
+  // (values first: centroid rows requested just before can arrive meanwhile)
+  auto dequant = [&](int tile, const Pre& c, int kb, int vbuf, auto rag) {
+    dequant_v(tile, c, kb, vbuf, rag);
+    dequant_k(tile, c, kb, rag);
   };
 
   // ---- S^T = Khat Q^T for the 64 tokens of key buffer kb, row r of slab
@@ -581,6 +602,11 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
     const _Float16* kh = khi + kb * KBUF;
     const _Float16* kl = klo + kb * LBUF;
     if (R > 0) {
+      h8 qp[kNT];
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+        qp[nt] = QPL ? *reinterpret_cast<const h8*>(&qpl[((wave * kNT + nt) * 16 + c16) * 16 + (g == 1 ? 8 : 0)])
+                     : qpr[nt];
       // row slab_token(t, c16) of the coefficient tile (k 0..23)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -743,8 +769,9 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
   // buffer is rewritten two phases after its last read (two buffers) and
   // a value buffer four (three buffers).  The first group (threads
   // 0..255) stages the parameter words, two tiles ahead.  Packed codes are
-  // requested a matrix phase before their vector phase, which first asks
-  // for the centroid rows they index and forms P while those arrive.  (A wave whose rows
+  // requested a matrix phase before their vector phase, which forms P, asks
+  // for the centroid rows they index and dequantises values while those
+  // arrive.  (A wave whose rows
   // are all past the end only dequantises and keeps the barriers.)
   auto phase = [&]() {
     __syncthreads();
@@ -789,7 +816,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
         __builtin_amdgcn_s_setprio(1);
         qk(k & 1, sc, std::integral_constant<bool, KM != 0>{}, cst);
         pv((k + 2) % 3, pb);
-        mfma_read_order<(R > 0 ? 4 : 0) + (KM != 0 ? 8 : 5) * NKS + 2 * (NDT + NMU), 6>();
+        mfma_read_order<(R > 0 ? (QPL ? 6 : 4) : 0) + (KM != 0 ? 8 : 5) * NKS + 2 * (NDT + NMU), 6>();
         __builtin_amdgcn_s_setprio(0);
         if (KM == 0) {
 #pragma unroll
@@ -797,8 +824,8 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
         }
       }
       phase();   // ---- vector phase k
-      prefetch_cent(cur);   // its index arrived during the matrix phase
       if (live) softmax(sc, bias, pb, 0, std::false_type{});
+      prefetch_cent(cur);   // (its index arrived during the matrix phase)
       if (dq < nfull) dequant(tile_begin + dq, cur, dq & 1, dq % 3, std::false_type{});
       if (!flip && k + 2 < nfull) store_params(tile_begin + k + 2, par);
       load_codes(min(tile_begin + dq + 1, last), cur, std::false_type{});
