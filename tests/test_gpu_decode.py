@@ -149,6 +149,31 @@ def test_llm_decode_full_size_sampled():
     print(f"full-size decode worst |delta| {worst:.3e}")
 
 
+@pytest.mark.slow
+def test_decode_long_ragged_sampled():
+    """Many (sequence, kv head) groups over a long, ragged context (16 x 8
+    heads, 16421 tokens: 256 full windows and a 37-token tail in the last
+    split), in the MFMA decode's launch configuration; sampled groups
+    against the oracle."""
+    T = 16421
+    d = synth.llm_decode(T=T)
+    B, H = d["B"], d["Hkv"]
+    c = kv.KVCache(B, H, 128, (T + 63) // 64 * 64)
+    kv.kv_quantize_append(c, dev_bf16(d["K"]), dev_bf16(d["V"]), 0)
+    qd = dev_bf16(d["q"])
+    out = kv.attn_int2_decode(c, T, qd, 1 / math.sqrt(128))
+    torch.cuda.synchronize()
+    g = to_oracle(c)
+    got = out.cpu().numpy()
+    q64 = synth.bf16_bits_to_f32(d["q"]).astype(np.float64)
+    for b, h in [(0, 0), (7, 3), (15, 7)]:
+        gs = g.slice_bh(b, h)
+        qs = q64[b:b + 1, 4 * h:4 * h + 4].reshape(1, 1, 4, 128)
+        ref, _ = gs.attention(np.ascontiguousarray(qs), T, 1 / math.sqrt(128))
+        err = np.abs(got[b, 4 * h:4 * h + 4] - ref[0, 0]).max()
+        assert err <= TOL, f"b={b} h={h} err {err}"
+
+
 def test_window_prefix_and_rewind():
     """Window keys under the header's length contract: after appends past a
     window boundary, attention over a prefix of whole windows reads only
