@@ -4,43 +4,49 @@
 // Block = 8 waves x 32 query rows (256 rows) of one (sequence, query head)
 // and one range of cached tokens, which stream through in 64-token tiles.
 // Each thread dequantises 16 keys and 16 values of a tile straight from its
-// registers into fp16 LDS tiles (keys row-major, values transposed with the
-// tokens in the order the PV operand reads them).  A 2-bit code enters the
-// arithmetic as the exact fp16 value base + code (code_operand.h), so a
-// dequantised element is one fma.
+// registers into fp16 LDS tiles.  A code dword pairs codes i and i + 8 of a
+// packed word (code_operand.h: base + code, exact in fp16), so key channels
+// and value tokens are stored in that pairing: key operand position
+// 16 w + 2 p + e holds channel 16 w + p + 8 e (the queries are loaded in the
+// same order), and the score tiles and the PV k order pair tokens u, u + 8
+// (slab_token, pv_pos).
 //   S^T = Khat Q^T    A = key tile from LDS, B = the wave's queries (kept in
 //                     registers for the whole loop);
-//   O^T += Vc^T P^T   A = the centred value tile, B = P straight from the
-//                     score registers (the token order inside each 32-token
-//                     k-step is permuted so that every lane already holds
-//                     the eight P values it supplies);
+//   O^T += Vc^T P^T   A = the value tile, B = P straight from the score
+//                     registers (every lane already holds the eight P values
+//                     it supplies);
 //   L   += M^T P^T    A = a 16-row tile of row sums: row 0 all ones (the
 //                     softmax denominator), the next rows each value
 //                     group's level-1 point mu = z + s per (token, group)
 //                     as fp16 hi and lo parts (per modality for
 //                     per-modality rotations), so sum_t p_t mu_t comes out
 //                     exact to fp32.
-// Precision: every key enters as fp16 hi + lo (Khat = hi + lo, both fp16,
-// multiplied twice), exact to fp32 whatever the key range.  A value enters
-// as (code - 1) s in {-s, 0, s, 2s}, exact in fp16, and z + s comes from
-// the row sums above, so the values carry no rounding at all.  The PSAC
-// term uses k 0..23 of its k-step as a_hi q'_hi + a_hi q'_lo + a_lo q'_hi.
+// Precision.  A value enters as (code - 1) s in {-s, 0, s, 2s}: one packed
+// fp16 add and one packed multiply per two values, both exact, with z + s
+// from the row sums above, so the values carry no rounding.  Window keys
+// are (code - 1) s as well (exact, one MFMA pass) and the channels' level-1
+// points z + s enter each row as a bias: a 16-row A tile holding their hi
+// and lo parts gives sum_c q_c (z_c + s_c) from 8 small MFMAs per tile.
+// Centroid keys (centroid + residual, fp32) enter as fp16 hi + lo (two
+// passes), the lo part one v_fma_mixlo/mixhi per half.  The PSAC term uses
+// k 0..23 of one more k-step as a_hi q'_hi + a_hi q'_lo + a_lo q'_hi.
 // Probabilities are fp16 (their rounding multiplies v - o, not v).
 // Softmax is base 2 with a lazy reference maximum: a row's m moves only
 // when a score passes it by more than 2^8; each lane tests its own scores,
 // and the cross-lane row maximum and the rescale run in a wave-uniform
 // branch that is rarely taken.
-// PSAC ([QWM] 2) adds (U^T q) . a as one more MFMA k-step.
+// PSAC ([QWM] 2) adds (U^T q) . a as that extra MFMA k-step.
 // Rotated values ([OKV]) are rotated back in registers at the end; with
 // per-modality rotations each value takes its modality's signs first.
 //
-// Software pipeline, one barrier per tile: while a wave multiplies QK of
-// tile j it dequantises its share of tile j + 1 into the other key buffer
-// and the next of three value buffers, and while it multiplies PV of tile
-// j - 1 it forms P of tile j; packed codes and parameters are requested
-// two tiles ahead.  A ragged last tile runs unpipelined after the others.
-// When the row blocks alone would not fill the device, the cached tokens
-// are split over blocks and a merge kernel combines the partial (o, m, l).
+// Schedule: the two waves of each SIMD (w and w + 4) alternate a matrix
+// phase (QK of tile k, PV of tile k - 1) and a vector phase (softmax of tile
+// k, a share of a later tile's dequantisation, the next loads), one group
+// a phase behind the other, with a barrier per phase; the matrix phase's
+// LDS reads are ordered ahead of their MFMAs.  A ragged last tile runs
+// unpipelined after the others.  When the row blocks alone would not fill
+// the device, the cached tokens are split over blocks and a merge kernel
+// combines the partial (o, m, l).
 #include <type_traits>
 
 #include "code_operand.h"
