@@ -60,6 +60,8 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Fourth word of a raw buffer resource (32-bit data format).
+constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kWaves = 8;
 constexpr int kNT = 2;                       // 16-row query tiles per wave
 constexpr int kBM = kWaves * kNT * 16;      // query rows per block
@@ -346,16 +348,36 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
   // this thread's packed words of a tile: codes, centroid index, PSAC
   // coefficients.  RAG (the ragged last tile): rows past the length read as
   // 0, so they dequantise to finite values; full tiles load unconditionally.
+  // Buffer views of this (sequence, kv head)'s rows: per-thread offsets
+  // stay fixed, a tile's offset goes in the scalar offset, and no 64-bit
+  // address arithmetic is left in the loop (reads past a view return 0).
+  const auto rkc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.kcodes + bh * a.Tcap * (D / 4)), (short)0,
+                                                     a.Tcap * (D / 4), kRsrcWord3);
+  const auto rki = __builtin_amdgcn_make_buffer_rsrc((void*)(a.kidx + (KM != 0 ? bh * a.Tcap : 0)), (short)0,
+                                                     KM != 0 ? a.Tcap : 0, kRsrcWord3);
+  const auto rvc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.vcodes + bh * (a.Tcap / 64) * (int64_t)D * 16), (short)0, (a.Tcap / 64) * D * 16, kRsrcWord3);
+  const auto rvp = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vparams + bh * a.Tcap * NG), (short)0,
+                                                     a.Tcap * NG * 4, kRsrcWord3);
+  const auto rkp = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.kparams + (KM == 0 ? bh * (a.Tcap / 64) * D : bh * a.Tcap * NG)), (short)0,
+      (KM == 0 ? (a.Tcap / 64) * D : a.Tcap * NG) * 4, kRsrcWord3);
+  const auto rmd = __builtin_amdgcn_make_buffer_rsrc((void*)(VM == 2 ? a.vmodal + (int64_t)b * a.Tcap : a.vmodal),
+                                                     (short)0, VM == 2 ? a.Tcap : 0, kRsrcWord3);
+  const auto rce = __builtin_amdgcn_make_buffer_rsrc((void*)(KM != 0 ? a.cent + bh * a.C * D : a.cent), (short)0,
+                                                     KM != 0 ? a.C * D * 4 : 0, kRsrcWord3);
+  const int pi = tid % (64 * NG);   // (token, group) parameter word of this thread
+  // this thread's packed words of a tile: codes, centroid index, PSAC
+  // coefficients.  RAG (the ragged last tile): rows past the length read as
+  // 0, so they dequantise to finite values; full tiles load unconditionally.
   auto load_codes = [&](int tile, Pre& f, auto rag) {
     constexpr bool RAG = decltype(rag)::value;
     const int t0 = tile * 64;
     const int64_t rowbase = bh * a.Tcap + t0;
-    f.kcw = has_k ? reinterpret_cast<const uint32_t*>(a.kcodes + rowbase * (D / 4))[tk * KW + kw] : 0u;
-    f.vcw = has_v ? reinterpret_cast<const uint32_t*>(
-                        a.vcodes + (bh * (a.Tcap / 64) + tile) * (int64_t)D * 16)[tid]
-                  : 0u;
+    f.kcw = has_k ? __builtin_amdgcn_raw_buffer_load_b32(rkc, (tk * KW + kw) * 4, t0 * (D / 4), 0) : 0u;
+    f.vcw = has_v ? __builtin_amdgcn_raw_buffer_load_b32(rvc, tid * 4, tile * D * 16, 0) : 0u;
     if (KM != 0) {
-      f.ix = has_k ? (int)a.kidx[rowbase + tk] : 0;
+      f.ix = has_k ? (int)__builtin_amdgcn_raw_buffer_load_b8(rki, tk, t0, 0) : 0;
       if (RAG && t0 + tk >= n) f.ix = 0;
     }
     f.cf = 0u;
@@ -381,31 +403,27 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
   auto load_params = [&](int tile, Par& f, auto rag) {
     constexpr bool RAG = decltype(rag)::value;
     const int t0 = tile * 64;
-    const int64_t rowbase = bh * a.Tcap + t0;
-    const int pi = tid % (64 * NG);   // (token, group) parameter word
-    f.vp = a.vparams[rowbase * NG + pi];
+    f.vp = __builtin_amdgcn_raw_buffer_load_b32(rvp, pi * 4, t0 * NG * 4, 0);
     if (RAG && t0 + pi / NG >= n) f.vp = 0u;
     if (KM == 0) {
-      f.kp = (RAG && tile >= n_full) ? 0u : a.kparams[(bh * (a.Tcap / 64) + tile) * D + tid % D];
+      f.kp = (RAG && tile >= n_full) ? 0u : __builtin_amdgcn_raw_buffer_load_b32(rkp, (tid % D) * 4, tile * D * 4, 0);
     } else {
-      f.kp = a.kparams[rowbase * NG + pi];
+      f.kp = __builtin_amdgcn_raw_buffer_load_b32(rkp, pi * 4, t0 * NG * 4, 0);
       if (RAG && t0 + pi / NG >= n) f.kp = 0u;
     }
     f.md = 0u;
-    if (VM == 2 && tid < 16)
-      f.md = reinterpret_cast<const uint32_t*>(a.vmodal + (int64_t)b * a.Tcap + t0)[tid];
+    if (VM == 2 && tid < 16) f.md = __builtin_amdgcn_raw_buffer_load_b32(rmd, tid * 4, t0, 0);
   };
   // centroid rows need the index, so they are requested one step later
   auto prefetch_cent = [&](Pre& f) {
     if (KM != 0 && has_k) {
-      const float* cr = a.cent + (bh * a.C + f.ix) * D + 16 * kw;
+      const int co = (f.ix * D + 16 * kw) * 4;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float4 c4 = *reinterpret_cast<const float4*>(cr + 4 * j);
-        f.cv[4 * j] = c4.x;
-        f.cv[4 * j + 1] = c4.y;
-        f.cv[4 * j + 2] = c4.z;
-        f.cv[4 * j + 3] = c4.w;
+        // bit-cast the whole vector: this compiler reads element 0 for a
+        // bit_cast of one subscripted vector element
+        const float4 c4 = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rce, co + 16 * j, 0, 0));
+        f.cv[4 * j] = c4.x; f.cv[4 * j + 1] = c4.y; f.cv[4 * j + 2] = c4.z; f.cv[4 * j + 3] = c4.w;
       }
     }
   };
