@@ -426,14 +426,28 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
 // row finish the sum.  (The permlane swap builtins would save two
 // exchanges, but this compiler merges their two results when both feed
 // one expression.)
+// Lane exchanges without the generic shuffle's per-call index arithmetic:
+// xor 16 is a swizzle inside each 32-lane half (bit mode: and 0x1F, xor
+// 0x10), xor 32 and broadcasts are bpermutes with byte addresses.
+KVQ_DEV float lane_xor16(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+KVQ_DEV float lane_xor32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(((int)(threadIdx.x & 63) ^ 32) << 2,
+                                                                __builtin_bit_cast(int, v)));
+}
+KVQ_DEV float lane_read(float v, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
+}
+
 KVQ_DEV float wave_sum4(const float v[4]) {
   const int lane = threadIdx.x & 63;
   const bool hi32 = (lane & 32) != 0, hi16 = (lane & 16) != 0;
   const float k0 = hi32 ? v[2] : v[0], k1 = hi32 ? v[3] : v[1];
   const float s0 = hi32 ? v[0] : v[2], s1 = hi32 ? v[1] : v[3];
-  const float a0 = k0 + __shfl_xor(s0, 32, 64), a1 = k1 + __shfl_xor(s1, 32, 64);
+  const float a0 = k0 + lane_xor32(s0), a1 = k1 + lane_xor32(s1);
   const float k = hi16 ? a1 : a0, sn = hi16 ? a0 : a1;
-  float y = k + __shfl_xor(sn, 16, 64);
+  float y = k + lane_xor16(sn);
   y += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), 0x128, 0xF, 0xF, false));
   y += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), 0x124, 0xF, 0xF, false));
   y += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), 0x122, 0xF, 0xF, false));
@@ -459,13 +473,13 @@ KVQ_DEV float wave_sum16_at(const float v[16], int jsel) {
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     const float keep = b5 ? v[m + 8] : v[m], send = b5 ? v[m] : v[m + 8];
-    a[m] = keep + __shfl_xor(send, 32, 64);
+    a[m] = keep + lane_xor32(send);
   }
   float c4[4];
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const float keep = b4 ? a[n + 4] : a[n], send = b4 ? a[n] : a[n + 4];
-    c4[n] = keep + __shfl_xor(send, 16, 64);
+    c4[n] = keep + lane_xor16(send);
   }
   float c2[2];
 #pragma unroll
@@ -479,17 +493,19 @@ KVQ_DEV float wave_sum16_at(const float v[16], int jsel) {
                        0, __builtin_bit_cast(int, send), 0x141, 0xF, 0xF, false));   // row_half_mirror
   y += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
   y += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
-  return __shfl(y, 4 * jsel, 64);
+  return lane_read(y, 4 * jsel);
 }
 
 __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(const DecodeArgs a) {
   constexpr int D = 128, G = 4, MAXW = kDecodeMaxWindows / 4;
   __shared__ float qs[D][G];                                   // q * scale * log2 e
   // A wave's LDS accesses spread over the 64 banks: qb heads are padded
-  // by 4 dwords, pb columns by 4; sl stores token t of head h at t ^ 16h.
-  // After pass 2 a wave's sl region holds its partial output.
+  // by 4 dwords, pb columns by 4.  sl is unpadded (the four heads' logit
+  // writes share banks, but each write is one base register plus an
+  // immediate offset).  After pass 2 a wave's sl region holds its partial
+  // output.
   __shared__ __align__(16) uint32_t qb[4][4][132];             // [wave][head][(hi,lo) g ks] 8 halfs
-  __shared__ __align__(16) float sl[4][MAXW][G][kWave];        // [wave][slot][head][token ^ 16 head]
+  __shared__ __align__(16) float sl[4][MAXW][G][kWave];        // [wave][slot][head][token]
   __shared__ __align__(16) _Float16 pb[4][16][72];             // [wave][col][(g kk) 8 halfs]
   __shared__ float wm[4][G], wlv[4][G];
 
@@ -600,7 +616,7 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(const DecodeArgs a)
     // row r of bsum holds the bias of head r; it enters the hi columns
     // (0..3) of the accumulator only
     const float bsum = wave_sum4(bias);
-    const float bl = __shfl(bsum, (c16 & 3) * 16, 64);
+    const float bl = lane_read(bsum, (c16 & 3) * 16);
     const float bc = c16 < 4 ? bl : 0.0f;
     const f4 binit = f4{bc, bc, bc, bc};
     wave_lds_sync();
@@ -636,7 +652,7 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(const DecodeArgs a)
       for (int i = 0; i < 4; ++i) v4[i] += row_shl4(v4[i]);
       mx = fmaxf(fmaxf(fmaxf(mx, v4[0]), v4[1]), fmaxf(v4[2], v4[3]));
       if (c16 < 4)
-        *reinterpret_cast<f4*>(&sl[wave][slot][c16][(ts * 16 + 4 * g) ^ (16 * c16)]) = f4{v4[0], v4[1], v4[2], v4[3]};
+        *reinterpret_cast<f4*>(&sl[wave][slot][c16][ts * 16 + 4 * g]) = f4{v4[0], v4[1], v4[2], v4[3]};
     }
   };
 
@@ -677,7 +693,7 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(const DecodeArgs a)
     }
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float p = __builtin_amdgcn_exp2f(sl[wave][slot][hh][lane ^ (16 * hh)] - M[hh]);
+      const float p = __builtin_amdgcn_exp2f(sl[wave][slot][hh][lane] - M[hh]);
       l_lane[hh] += p;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -723,8 +739,8 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(const DecodeArgs a)
     if (k < n_full) window_logits(kbuf[k], k);
   }
   // lane c16 < 4 of each row holds head c16: reduce across the four rows
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = fmaxf(mx, lane_xor16(mx));
+  mx = fmaxf(mx, lane_xor32(mx));
 #pragma unroll
   for (int hh = 0; hh < G; ++hh)
     M[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), hh));
@@ -751,7 +767,7 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(const DecodeArgs a)
     }
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      sl[wave][n_full][hh][lane ^ (16 * hh)] = lg[hh];
+      sl[wave][n_full][hh][lane] = lg[hh];
       M[hh] = fmaxf(M[hh], wave_max(lg[hh]));
     }
   }

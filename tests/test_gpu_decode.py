@@ -100,6 +100,36 @@ def test_window_decode_reused_workspace():
         assert torch.equal(lse_a, lse_b), f"n={n}"
 
 
+def test_window_decode_uninitialised_workspace():
+    """A workspace full of random bytes, reused across calls whose split
+    counts differ, gives the fresh-workspace results bit for bit (bf16
+    output and lse included), and the oracle's within tolerance: nothing in
+    it is read before this call writes it."""
+    d = synth.llm_decode(B=3, Hkv=2, Hq=8, D=128, T=5000)
+    c = kv.KVCache(3, 2, 128, 5056, value_mode=kv.VAL_HADAMARD)
+    o = oracle_like(c)
+    kv.kv_quantize_append(c, dev_bf16(d["K"]), dev_bf16(d["V"]), 0)
+    o.append(d["K"], d["V"], 0)
+    qd = dev_bf16(d["q"])
+    q64 = synth.bf16_bits_to_f32(d["q"]).astype(np.float64)
+    ws = kv.decode_workspace(c, 8, 5000)
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, generator=gen))
+    g = to_oracle(c)
+    for n in (5000, 777, 64, 5000, 4096):
+        lse_a = torch.empty(24, dtype=torch.float32, device="cuda")
+        lse_b = torch.empty(24, dtype=torch.float32, device="cuda")
+        a = kv.attn_int2_decode(c, n, qd, 1 / math.sqrt(128), out_dtype=torch.bfloat16, lse=lse_a, workspace=ws)
+        b = kv.attn_int2_decode(c, n, qd, 1 / math.sqrt(128), out_dtype=torch.bfloat16, lse=lse_b)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), f"n={n}"
+        assert torch.equal(lse_a, lse_b), f"n={n}"
+        ref, rlse = g.attention(q64.reshape(3, 1, 8, 128), n, 1 / math.sqrt(128))
+        err = np.abs(a.float().cpu().numpy().astype(np.float64) - ref[:, 0])
+        assert np.all(err <= TOL + np.abs(ref[:, 0]) * 2.0 ** -8), f"n={n}: max err {err.max():.3e}"
+        assert np.abs(lse_a.cpu().numpy().reshape(3, 8) - rlse[:, :, 0]).max() < 1e-3, f"n={n}"
+
+
 @pytest.mark.parametrize("mode,R,had,fmt", [(kv.KEY_CENTROID, 0, True, 0), (kv.KEY_CENTROID_QSAC, 8, True, 0),
                                             (kv.KEY_CENTROID_QSAC, 8, False, 0),
                                             (kv.KEY_CENTROID_QSAC, 8, True, kv.PSAC_INT8)])
