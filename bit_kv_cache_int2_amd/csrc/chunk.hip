@@ -848,8 +848,8 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
         }
       }
       phase();   // ---- vector phase k
-      if (live) softmax(sc, bias, pb, 0, std::false_type{});
       prefetch_cent(cur);   // (its index arrived during the matrix phase)
+      if (live) softmax(sc, bias, pb, 0, std::false_type{});
       if (dq < nfull) dequant(tile_begin + dq, cur, dq & 1, dq % 3, std::false_type{});
       if (!flip && k + 2 < nfull) store_params(tile_begin + k + 2, par);
       load_codes(min(tile_begin + dq + 1, last), cur, std::false_type{});
