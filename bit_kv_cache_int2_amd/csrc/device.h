@@ -102,6 +102,28 @@ KVQ_DEV uint32_t q2_code(float x, const Q2& q) {
   return (up ? 2u : 0u) + (uint32_t)(x >= (up ? q.t2 : q.t0));
 }
 
+// Value of lane (lane ^ M) in a wave of 64, without the generic shuffle's
+// per-call index arithmetic: xor 1 and 2 are DPP quad permutes, xor 4, 8
+// and 16 swizzles inside each 32-lane half (bit mode: and 0x1F, xor M),
+// xor 32 a bpermute.  Every lane must be active.
+template <int M>
+KVQ_DEV uint32_t lane_xor(uint32_t v) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "lane_xor: power of two below 64");
+  if constexpr (M == 1) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+  } else if constexpr (M == 2) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+  } else if constexpr (M < 32) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (M << 10) | 0x1F);
+  } else {
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(((int)(threadIdx.x & 63) ^ 32) << 2, (int)v);
+  }
+}
+template <int M>
+KVQ_DEV float lane_xor(float v) {
+  return __uint_as_float(lane_xor<M>(__float_as_uint(v)));
+}
+
 // Wave-level reductions (64 lanes) with butterfly shuffles.
 KVQ_DEV float wave_max(float v) {
 #pragma unroll

@@ -9,11 +9,18 @@
 //    in registers (three in-lane butterfly stages, then one xor-shuffle
 //    stage per remaining bit).
 //  * centroid keys ([QWM] 1): the values here, the keys in assign.hip.
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
 namespace kvq {
 namespace {
+
+// Fourth word of a raw buffer resource (32-bit data format), and the
+// non-temporal cache policy of streamed input rows.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kStreamPolicy = 2;
 
 
 // INT2 codes by sign bits.  The kernels hold each threshold negated,
@@ -65,15 +72,20 @@ KVQ_DEV void wht_row(float (&x)[8]) {
     }
   }
   const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int s = 1; s < D / 8; s <<= 1) {
-    const bool upper = (lane & s) != 0;
+  auto stage = [&](auto sc) {
+    constexpr int S = decltype(sc)::value;
+    const bool upper = (lane & S) != 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const float o = __shfl_xor(x[k], s, 64);
+      const float o = lane_xor<S>(x[k]);
       x[k] = upper ? (o - x[k]) : (x[k] + o);
     }
-  }
+  };
+  stage(std::integral_constant<int, 1>{});
+  stage(std::integral_constant<int, 2>{});
+  stage(std::integral_constant<int, 4>{});
+  if constexpr (D / 8 > 8) stage(std::integral_constant<int, 8>{});
+  static_assert(D / 8 <= 16, "wht_row: at most four cross-lane stages");
   const float c = __uint_as_float(D == 128 ? 0x3DB504F3u : 0x3E000000u);
 #pragma unroll
   for (int k = 0; k < 8; ++k) x[k] = x[k] * c;
@@ -133,20 +145,43 @@ __global__ __launch_bounds__(256) void tile_append_kernel(
   const int64_t row0 = ((int64_t)b * n_new - cur_len) * H + h;   // row index of token p: row0 + p * H
   uint4 vraw[NP], kraw[NP];
   uint32_t vneg[NP];   // per-modality rotations: sign bits of this row's 8 channels
+  if (cur_len <= wb && wb + kWindow <= end) {
+    // every row of the window is new: buffer views from token wb's row,
+    // a fixed per-lane offset and one scalar offset per row step
+    const int64_t rw = (row0 + (int64_t)wb * H) * D;
+    const int span = kWindow * H * D * 2;
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vin + rw), (short)0, span, kRsrcWord3);
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kin + rw), (short)0, span, kRsrcWord3);
+    const int vo = (r0 * H * D + j * 8) * 2;
 #pragma unroll
-  for (int k = 0; k < NP; ++k) {
-    const int p = wb + r0 + RPP * k;
-    const int pc = min(max(p, t_lo), t_hi - 1);
-    vraw[k] = ld_stream(vin + (row0 + (int64_t)pc * H) * D + j * 8);
-    vneg[k] = 0u;
-    if (VM == 2) {
-      const int m = min((int)vmodal[(int64_t)b * Tcap + pc], M - 1);
-      vneg[k] = (vsigns[((int64_t)h * M + m) * (D / 32) + (8 * j) / 32] >> ((8 * j) & 31)) & 0xFFu;
+    for (int k = 0; k < NP; ++k) {
+      const int so = k * RPP * H * D * 2;
+      const auto vv = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, so, kStreamPolicy);
+      const auto kv = __builtin_amdgcn_raw_buffer_load_b128(rk, vo, so, kStreamPolicy);
+      vraw[k] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+      kraw[k] = make_uint4(kv[0], kv[1], kv[2], kv[3]);
+      vneg[k] = 0u;
+      if (VM == 2) {
+        const int m = min((int)vmodal[(int64_t)b * Tcap + wb + r0 + RPP * k], M - 1);
+        vneg[k] = (vsigns[((int64_t)h * M + m) * (D / 32) + (8 * j) / 32] >> ((8 * j) & 31)) & 0xFFu;
+      }
     }
-    const int pk = full ? p : pc;
-    const uint16_t* src = (pk < cur_len) ? tail + (int64_t)(pk & (kWindow - 1)) * D
-                                         : kin + (row0 + (int64_t)pk * H) * D;
-    kraw[k] = ld_stream(src + j * 8);
+  } else {
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const int p = wb + r0 + RPP * k;
+      const int pc = min(max(p, t_lo), t_hi - 1);
+      vraw[k] = ld_stream(vin + (row0 + (int64_t)pc * H) * D + j * 8);
+      vneg[k] = 0u;
+      if (VM == 2) {
+        const int m = min((int)vmodal[(int64_t)b * Tcap + pc], M - 1);
+        vneg[k] = (vsigns[((int64_t)h * M + m) * (D / 32) + (8 * j) / 32] >> ((8 * j) & 31)) & 0xFFu;
+      }
+      const int pk = full ? p : pc;
+      const uint16_t* src = (pk < cur_len) ? tail + (int64_t)(pk & (kWindow - 1)) * D
+                                           : kin + (row0 + (int64_t)pk * H) * D;
+      kraw[k] = ld_stream(src + j * 8);
+    }
   }
   // value tile words.  A tile that starts fresh (no earlier tokens in it) is
   // assembled from whole bytes; otherwise the words start from the codes of
@@ -182,10 +217,10 @@ __global__ __launch_bounds__(256) void tile_append_kernel(
       mn = fminf(mn, x[e]);
       mx = fmaxf(mx, x[e]);
     }
-    mn = fminf(mn, __shfl_xor(mn, 1, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-    mn = fminf(mn, __shfl_xor(mn, 2, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+    mn = fminf(mn, lane_xor<1>(mn));
+    mx = fmaxf(mx, lane_xor<1>(mx));
+    mn = fminf(mn, lane_xor<2>(mn));
+    mx = fmaxf(mx, lane_xor<2>(mx));
     const Q2 q = q2_make(mn, mx);
     const NegThr u = neg_thresholds(q);
     uint32_t acc = ~0u;                      // channel 8j+e at bits [2e, 2e+1] of ~acc
@@ -204,10 +239,10 @@ __global__ __launch_bounds__(256) void tile_append_kernel(
         return (t | (t << 6)) & 0x03030303u;
       };
       uint32_t v0 = spread(bits & 0xFFu) << (2 * i), v1 = spread(bits >> 8) << (2 * i);
-      v0 |= __shfl_xor(v0, 16, 64);
-      v1 |= __shfl_xor(v1, 16, 64);
-      v0 |= __shfl_xor(v0, 32, 64);
-      v1 |= __shfl_xor(v1, 32, 64);
+      v0 |= lane_xor<16>(v0);
+      v1 |= lane_xor<16>(v1);
+      v0 |= lane_xor<32>(v0);
+      v1 |= lane_xor<32>(v1);
       uint8_t* vb = reinterpret_cast<uint8_t*>(&vt[0][0]);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -242,11 +277,14 @@ __global__ __launch_bounds__(256) void tile_append_kernel(
         mx[e] = fmaxf(mx[e], kx[k][e]);
       }
       // rows held by this wave: lanes with the same j differ in bits >= log2(LPR)
-#pragma unroll
-      for (int o = LPR; o < 64; o <<= 1) {
-        mn[e] = fminf(mn[e], __shfl_xor(mn[e], o, 64));
-        mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], o, 64));
+      if constexpr (LPR <= 8) {
+        mn[e] = fminf(mn[e], lane_xor<8>(mn[e]));
+        mx[e] = fmaxf(mx[e], lane_xor<8>(mx[e]));
       }
+      mn[e] = fminf(mn[e], lane_xor<16>(mn[e]));
+      mx[e] = fmaxf(mx[e], lane_xor<16>(mx[e]));
+      mn[e] = fminf(mn[e], lane_xor<32>(mn[e]));
+      mx[e] = fmaxf(mx[e], lane_xor<32>(mx[e]));
     }
     if (lane < LPR) {
 #pragma unroll
