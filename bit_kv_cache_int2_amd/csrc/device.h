@@ -38,6 +38,7 @@ KVQ_DEV float f16_bits_to_f32(uint32_t b) {
 }
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 // 16-byte load of data read exactly once (streamed inputs): non-temporal, so
 // it does not displace reusable lines from the caches.
