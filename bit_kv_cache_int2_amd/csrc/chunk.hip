@@ -793,9 +793,9 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(const ChunkArgs a) {
   // buffer is rewritten two phases after its last read (two buffers) and
   // a value buffer four (three buffers).  The first group (threads
   // 0..255) stages the parameter words, two tiles ahead.  Packed codes are
-  // requested a matrix phase before their vector phase, which forms P, asks
-  // for the centroid rows they index and dequantises values while those
-  // arrive.  (A wave whose rows
+  // requested a matrix phase before their vector phase, which first asks
+  // for the centroid rows they index, then forms P and dequantises values
+  // while those arrive.  (A wave whose rows
   // are all past the end only dequantises and keeps the barriers.)
   auto phase = [&]() {
     __syncthreads();
