@@ -504,9 +504,12 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(const DecodeArgs a)
   // writes share banks, but each write is one base register plus an
   // immediate offset).  After pass 2 a wave's sl region holds its partial
   // output.
-  __shared__ __align__(16) uint32_t qb[4][4][132];             // [wave][head][(hi,lo) g ks] 8 halfs
+  // qb (pass 1, two buffers) and pb (pass 2) share one region per wave.
+  __shared__ __align__(16) uint32_t qpb[4][2][4][132];
+  uint32_t (*const qb)[4][132] = qpb[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];   // [buf][head][(hi,lo) g ks] 8 halfs
   __shared__ __align__(16) float sl[4][MAXW][G][kWave];        // [wave][slot][head][token]
-  __shared__ __align__(16) _Float16 pb[4][16][72];             // [wave][col][(g kk) 8 halfs]
+  _Float16 (*const pb)[72] = reinterpret_cast<_Float16 (*)[72]>(&qpb[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)][0][0][0]);   // [col][(g kk) 8 halfs]
+  static_assert(sizeof(qpb[0]) >= 16 * 72 * sizeof(_Float16), "pb fits in a wave's share");
   __shared__ float wm[4][G], wlv[4][G];
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -597,8 +600,12 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(const DecodeArgs a)
   };
 
   float mx = -__builtin_inff();        // running max of head (lane % 4)
-  auto window_logits = [&](const KWin& cur, int slot) {
-    // fold the query into the window: qt hi/lo -> LDS, bias
+  // Pass 1 is pipelined one window deep: the query fold of window k + 1
+  // (q~ hi/lo into query buffer (k + 1) & 1, and its bias, whose lane
+  // exchanges are long-latency) is issued while the MFMAs of window k run.
+  // fold returns the accumulator's initial value for this lane: row r of
+  // the bias sum is head r's, and only the hi columns (0..3) take it.
+  auto fold = [&](const KWin& cur, int buf) -> float {
     const float sa = f16_bits_to_f32(cur.pa), za = f16_bits_to_f32(cur.pa >> 16);
     const float sb = f16_bits_to_f32(cur.pb), zb = f16_bits_to_f32(cur.pb >> 16);
     const float zca = __builtin_fmaf(-fbase, sa, za), zcb = __builtin_fmaf(-fbase, sb, zb);
@@ -609,23 +616,25 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(const DecodeArgs a)
       const float la = __builtin_fmaf(qa[hh], sa, -(float)hi[0]);
       const float lb = __builtin_fmaf(qbv[hh], sb, -(float)hi[1]);
       const auto lo = __builtin_amdgcn_cvt_pkrtz(la, lb);
-      qb[wave][hh][qg * 16 + qks * 4 + qi2] = __builtin_bit_cast(uint32_t, hi);
-      qb[wave][hh][64 + qg * 16 + qks * 4 + qi2] = __builtin_bit_cast(uint32_t, lo);
+      qb[buf][hh][qg * 16 + qks * 4 + qi2] = __builtin_bit_cast(uint32_t, hi);
+      qb[buf][hh][64 + qg * 16 + qks * 4 + qi2] = __builtin_bit_cast(uint32_t, lo);
       bias[hh] = __builtin_fmaf(qa[hh], zca, qbv[hh] * zcb);
     }
-    // row r of bsum holds the bias of head r; it enters the hi columns
-    // (0..3) of the accumulator only
     const float bsum = wave_sum4(bias);
     const float bl = lane_read(bsum, (c16 & 3) * 16);
-    const float bc = c16 < 4 ? bl : 0.0f;
+    return c16 < 4 ? bl : 0.0f;
+  };
+  // the logits of a window whose fold is in query buffer buf (already
+  // ordered before this read by a wave_lds_sync) into sl slot `slot`;
+  // `next` runs between the MFMAs' issue and the reads of their results
+  auto window_logits = [&](const KWin& cur, int buf, float bc, int slot, auto next) {
     const f4 binit = f4{bc, bc, bc, bc};
-    wave_lds_sync();
     // B operand columns: 0..3 hi parts of heads 0..3, 4..7 lo parts,
     // 8..15 copies (never read)
     h8 bq[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      bq[ks] = *reinterpret_cast<const h8*>(&qb[wave][c16 & 3][((c16 >> 2) & 1) * 64 + g * 16 + ks * 4]);
+      bq[ks] = *reinterpret_cast<const h8*>(&qb[buf][c16 & 3][((c16 >> 2) & 1) * 64 + g * 16 + ks * 4]);
     // four independent accumulator chains (token slabs ts), step-major
     f4 sacc[4] = {binit, binit, binit, binit};
 #pragma unroll
@@ -641,6 +650,7 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(const DecodeArgs a)
               as_h8(kw[ts][4 * hf], kw[ts][4 * hf + 1], kw[ts][4 * hf + 2], kw[ts][4 * hf + 3]),
               bq[2 * wd + hf], sacc[ts], 0, 0, 0);
     }
+    next();
     // hi + lo: column c16 < 4 adds column c16 + 4 (row shift by 4 lanes);
     // only lanes c16 < 4 carry logits from here on
 #pragma unroll
@@ -698,13 +708,13 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(const DecodeArgs a)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         pz[hh][q] = __builtin_fmaf(p, zc[q], pz[hh][q]);
-        pb[wave][4 * q + hh][g * 16 + kk * 8 + jj] = (_Float16)(p * sc[q]);
+        pb[4 * q + hh][g * 16 + kk * 8 + jj] = (_Float16)(p * sc[q]);
       }
     }
     wave_lds_sync();
     h8 bpv[2];
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) bpv[k2] = *reinterpret_cast<const h8*>(&pb[wave][c16][g * 16 + k2 * 8]);
+    for (int k2 = 0; k2 < 2; ++k2) bpv[k2] = *reinterpret_cast<const h8*>(&pb[c16][g * 16 + k2 * 8]);
 #pragma unroll
     for (int m0 = 0; m0 < 8; m0 += 4) {
       uint32_t vx[4][8];
@@ -728,6 +738,8 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(const DecodeArgs a)
   VWin vbuf[MAXW];
 #pragma unroll
   for (int k = 0; k < kKeyAhead; ++k) fetch_keys(w_first + 4 * k, kbuf[k], k < n_full);
+  float bc = 0.0f;
+  if (n_full > 0) bc = fold(kbuf[0], 0);
   // once the key stream is fully requested, the value stream starts
 #pragma unroll
   for (int k = 0; k < MAXW; ++k) {
@@ -736,7 +748,14 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(const DecodeArgs a)
       fetch_keys(w_first + 4 * kn, kbuf[kn], kn < n_full);
     else if (kn - MAXW < kValAhead)
       fetch_values(w_first + 4 * (kn - MAXW), vbuf[kn - MAXW], kn - MAXW < n_mine);
-    if (k < n_full) window_logits(kbuf[k], k);
+    if (k < n_full) {
+      wave_lds_sync();   // the fold of window k is in query buffer k & 1
+      float bc_next = 0.0f;
+      window_logits(kbuf[k], k & 1, bc, k, [&]() {
+        if (k + 1 < MAXW && k + 1 < n_full) bc_next = fold(kbuf[k + 1 < MAXW ? k + 1 : k], (k + 1) & 1);
+      });
+      bc = bc_next;
+    }
   }
   // lane c16 < 4 of each row holds head c16: reduce across the four rows
   mx = fmaxf(mx, lane_xor16(mx));
