@@ -426,16 +426,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
 // row finish the sum.  (The permlane swap builtins would save two
 // exchanges, but this compiler merges their two results when both feed
 // one expression.)
-// Lane exchanges without the generic shuffle's per-call index arithmetic:
-// xor 16 is a swizzle inside each 32-lane half (bit mode: and 0x1F, xor
-// 0x10), xor 32 and broadcasts are bpermutes with byte addresses.
-KVQ_DEV float lane_xor16(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
-}
-KVQ_DEV float lane_xor32(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(((int)(threadIdx.x & 63) ^ 32) << 2,
-                                                                __builtin_bit_cast(int, v)));
-}
+// Lane exchanges without the generic shuffle's per-call index arithmetic
+// (lane_xor in device.h); a broadcast from lane src is a bpermute.
 KVQ_DEV float lane_read(float v, int src) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
 }
@@ -445,9 +437,9 @@ KVQ_DEV float wave_sum4(const float v[4]) {
   const bool hi32 = (lane & 32) != 0, hi16 = (lane & 16) != 0;
   const float k0 = hi32 ? v[2] : v[0], k1 = hi32 ? v[3] : v[1];
   const float s0 = hi32 ? v[0] : v[2], s1 = hi32 ? v[1] : v[3];
-  const float a0 = k0 + lane_xor32(s0), a1 = k1 + lane_xor32(s1);
+  const float a0 = k0 + lane_xor<32>(s0), a1 = k1 + lane_xor<32>(s1);
   const float k = hi16 ? a1 : a0, sn = hi16 ? a0 : a1;
-  float y = k + lane_xor16(sn);
+  float y = k + lane_xor<16>(sn);
   y += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), 0x128, 0xF, 0xF, false));
   y += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), 0x124, 0xF, 0xF, false));
   y += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), 0x122, 0xF, 0xF, false));
@@ -473,13 +465,13 @@ KVQ_DEV float wave_sum16_at(const float v[16], int jsel) {
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     const float keep = b5 ? v[m + 8] : v[m], send = b5 ? v[m] : v[m + 8];
-    a[m] = keep + lane_xor32(send);
+    a[m] = keep + lane_xor<32>(send);
   }
   float c4[4];
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const float keep = b4 ? a[n + 4] : a[n], send = b4 ? a[n] : a[n + 4];
-    c4[n] = keep + lane_xor16(send);
+    c4[n] = keep + lane_xor<16>(send);
   }
   float c2[2];
 #pragma unroll
@@ -758,8 +750,8 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(const DecodeArgs a)
     }
   }
   // lane c16 < 4 of each row holds head c16: reduce across the four rows
-  mx = fmaxf(mx, lane_xor16(mx));
-  mx = fmaxf(mx, lane_xor32(mx));
+  mx = fmaxf(mx, lane_xor<16>(mx));
+  mx = fmaxf(mx, lane_xor<32>(mx));
 #pragma unroll
   for (int hh = 0; hh < G; ++hh)
     M[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), hh));
