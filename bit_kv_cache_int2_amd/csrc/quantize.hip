@@ -149,6 +149,11 @@ __global__ __launch_bounds__(256) void tile_append_kernel(
   const int64_t row0 = ((int64_t)b * n_new - cur_len) * H + h;   // row index of token p: row0 + p * H
   uint4 vraw[NP], kraw[NP];
   uint32_t vneg[NP];   // per-modality rotations: sign bits of this row's 8 channels
+  auto signs = [&](int tok) -> uint32_t {
+    if (VM != 2) return 0u;
+    const int m = min((int)vmodal[(int64_t)b * Tcap + tok], M - 1);
+    return (vsigns[((int64_t)h * M + m) * (D / 32) + (8 * j) / 32] >> ((8 * j) & 31)) & 0xFFu;
+  };
   if (cur_len <= wb && wb + kWindow <= end) {
     // every row of the window is new: buffer views from token wb's row,
     // a fixed per-lane offset and one scalar offset per row step
@@ -164,11 +169,7 @@ __global__ __launch_bounds__(256) void tile_append_kernel(
       const auto kv = __builtin_amdgcn_raw_buffer_load_b128(rk, vo, so, kStreamPolicy);
       vraw[k] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
       kraw[k] = make_uint4(kv[0], kv[1], kv[2], kv[3]);
-      vneg[k] = 0u;
-      if (VM == 2) {
-        const int m = min((int)vmodal[(int64_t)b * Tcap + wb + r0 + RPP * k], M - 1);
-        vneg[k] = (vsigns[((int64_t)h * M + m) * (D / 32) + (8 * j) / 32] >> ((8 * j) & 31)) & 0xFFu;
-      }
+      vneg[k] = signs(wb + r0 + RPP * k);
     }
   } else {
 #pragma unroll
@@ -176,11 +177,7 @@ __global__ __launch_bounds__(256) void tile_append_kernel(
       const int p = wb + r0 + RPP * k;
       const int pc = min(max(p, t_lo), t_hi - 1);
       vraw[k] = ld_stream(vin + (row0 + (int64_t)pc * H) * D + j * 8);
-      vneg[k] = 0u;
-      if (VM == 2) {
-        const int m = min((int)vmodal[(int64_t)b * Tcap + pc], M - 1);
-        vneg[k] = (vsigns[((int64_t)h * M + m) * (D / 32) + (8 * j) / 32] >> ((8 * j) & 31)) & 0xFFu;
-      }
+      vneg[k] = signs(pc);
       const int pk = full ? p : pc;
       const uint16_t* src = (pk < cur_len) ? tail + (int64_t)(pk & (kWindow - 1)) * D
                                            : kin + (row0 + (int64_t)pk * H) * D;
