@@ -175,9 +175,8 @@ int kv_quantize_append(const kvq_cache* cache, const void* k_bf16, const void* v
   if ((int64_t)cur_len + n_new > cache->layout.capacity) return KVQ_ECAPACITY;
   if (n_new == 0) return KVQ_OK;
   if (!k_bf16 || !v_bf16 || !aligned16(k_bf16) || !aligned16(v_bf16)) return KVQ_EINVAL;
-  // one block row per 64-token window the append touches (grid y)
-  const int64_t end = (int64_t)cur_len + n_new;
-  if ((end - 1) / KVQ_WINDOW - cur_len / KVQ_WINDOW + 1 > kvq::kMaxGridYZ) return KVQ_EUNSUPPORTED;
+  // the windows an append touches index grid x (up to 2^31 - 1 blocks), so
+  // the capacity limit of check_cache bounds them
   return hip_status(kvq::launch_quantize_append(cache, k_bf16, v_bf16, cur_len, n_new,
                                                 (hipStream_t)stream));
 }

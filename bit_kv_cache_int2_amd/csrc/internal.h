@@ -9,7 +9,7 @@
 
 namespace kvq {
 
-// Largest grid y / z dimension (sequences, heads, windows of one append).
+// Largest grid y / z dimension (sequences, heads; an append's windows index x).
 constexpr int kMaxGridYZ = 65535;
 // Largest cache capacity per (sequence, head): token-row offsets inside one
 // (sequence, head) stay within 32 bits.

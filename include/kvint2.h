@@ -242,8 +242,7 @@ int kvq_layout_check(const kvq_layout* L);
  * are overwritten): the append completes the unfinished window from the
  * tail, which holds the tokens of the last window only.
  * Errors: KVQ_EINVAL (null buffer a mode needs, cur_len < 0, n_new < 0),
- * KVQ_ECAPACITY (cur_len + n_new > capacity), KVQ_EUNSUPPORTED (the append
- * touches more than 65535 windows). n_new == 0 is a no-op. */
+ * KVQ_ECAPACITY (cur_len + n_new > capacity). n_new == 0 is a no-op. */
 int kv_quantize_append(const kvq_cache* cache, const void* k_bf16_dev,
                        const void* v_bf16_dev, int32_t cur_len, int32_t n_new,
                        void* stream);

@@ -295,3 +295,16 @@ def test_llm_decode_build_full_size_sampled():
         o.append(np.ascontiguousarray(d["K"][b:b + 1, :, h:h + 1]),
                  np.ascontiguousarray(d["V"][b:b + 1, :, h:h + 1]), 0)
         assert_cache_equal(g.slice_bh(b, h), o, T, f"b={b} h={h}")
+
+
+def test_append_of_more_than_65535_windows():
+    """One call that touches 65,601 windows (more than a 16-bit grid
+    dimension holds), after a 32-token append, so the call also completes
+    the first window from the tail and leaves 17 tokens in it; the whole
+    cache equals the oracle's."""
+    T = 65600 * 64 + 17
+    d = synth.llm_decode(B=1, Hkv=1, Hq=1, D=64, T=T)
+    c = kv.KVCache(1, 1, 64, ((T + 63) // 64) * 64)
+    o = oracle_like(c)
+    n = _append_both(c, o, d["K"], d["V"], [32, T - 32])
+    assert_cache_equal(to_oracle(c), o, n, "65601-window append")
