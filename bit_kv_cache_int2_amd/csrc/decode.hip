@@ -401,23 +401,24 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const DecodeArgs a)
 // shifts and eight and-ors.  Position i has base {16, 4, 64, 16, 4, 64, 16,
 // 4}[i].  All products are exact.
 //   S^T[token][head] = sum_c (base_c + code[token][c]) qt[head][c] with the
-//     hi and lo fp16 parts of qt = q * s_w * scale * log2 e stacked along K
-//     (the same code operand multiplies both); the window bias
-//     sum_c q_c (z_c - base_c s_c), the accumulator's initial value, adds
+//     hi and lo fp16 parts of qt = q * s_w * scale * log2 e in B columns
+//     0..3 and 4..7 (the same code operand multiplies both; columns 8..15
+//     are copies, never read), added after the MFMA, so lanes c16 < 4 of
+//     each 16-lane row hold the logits of head c16; the window bias
+//     sum_c q_c (z_c - base_c s_c), the hi columns' initial value, adds
 //     the zero points and removes the base term;
 //   O^T[c][col] = sum_t (base_t + code[t][c]) pt[t][col] with col = 4 group
 //     + head and pt = fp16(p * s_(t,group)); only the columns of a channel's
 //     own group are kept; the base term comes from one more MFMA against a
 //     constant operand holding the bases (same fp16 pt values), and
 //     sum_t p z_(t,group) is a per-lane fp32 sum.
-// B columns 4..15 of S^T hold copies of columns 0..3, so every lane's
-// accumulator holds logits of head (lane % 4).  A wave owns at most eight
-// windows of its split (every fourth one).  Pass 1 streams their key codes,
-// stores the logits (base 2) in LDS and takes the exact per-head maximum;
-// the partial window (bf16 key tail) of a sequence is scored with fp32 dot
-// products.  Pass 2 streams the value codes and accumulates p = 2^(l - m)
-// <= 1: no running rescale.  Each pass loads window w + 4 while it
-// computes window w.
+// A wave owns at most eight windows of its split (every fourth one).  Pass
+// 1 streams their key codes, stores the logits (base 2) in LDS and takes
+// the exact per-head maximum; the partial window (bf16 key tail) of a
+// sequence is scored with fp32 dot products.  Pass 2 streams the value
+// codes and accumulates p = 2^(l - m) <= 1: no running rescale.  Each pass
+// requests the wave's windows kKeyAhead (keys) or kValAhead (values) of its
+// own windows ahead of the one it computes.
 
 // Sums four per-lane values over the wave: afterwards every lane of row r
 // (lanes 16r .. 16r + 15) holds the total of v[r].  Each xor exchange
