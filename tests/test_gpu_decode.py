@@ -236,3 +236,85 @@ def test_window_prefix_and_rewind():
     o2 = oracle_like(c)
     o2.append(K2, V2, 0)
     _decode_check(c, o2, T, qd, q64, scale, "after the rewind")
+
+
+@pytest.mark.slow
+def test_decode_and_chunk_at_maximum_capacity():
+    """The largest capacity a cache takes (2^24 tokens per sequence and
+    head), filled by one append: 262,143 full windows, window w a copy of
+    window w % 7 of seven distinct ones, then a 17-token tail.  Every
+    window's cache bytes equal the oracle's for its copy, and decode (MFMA
+    path, 8,192 splits) and chunk attention over all 2^24 - 47 tokens equal
+    the oracle's merge of the seven window attentions, each weighted by its
+    number of copies, and the tail's."""
+    W, D, Hq = 7, 128, 4
+    T = (1 << 24) - 47
+    n_full, rem = T // 64, T % 64
+    d = synth.llm_decode(B=1, Hkv=1, Hq=Hq, D=D, T=W * 64 + rem)
+    t = np.arange(T)
+    w = t // 64
+    src = torch.from_numpy(np.where(w < n_full, (w % W) * 64 + t % 64, W * 64 + t - n_full * 64)).cuda()
+    del t, w
+    c = kv.KVCache(1, 1, D, 1 << 24)
+    kv.kv_quantize_append(c, dev_bf16(d["K"])[:, src].contiguous(), dev_bf16(d["V"])[:, src].contiguous(), 0)
+    torch.cuda.synchronize()
+    del src
+    torch.cuda.empty_cache()
+    # the oracle's cache of each distinct window, and of the tail alone
+    types = []
+    for j in range(W):
+        oj = oracle.Cache(1, 1, D, 64)
+        oj.append(np.ascontiguousarray(d["K"][:, 64 * j:64 * j + 64]),
+                  np.ascontiguousarray(d["V"][:, 64 * j:64 * j + 64]), 0)
+        types.append(oj)
+    ot = oracle.Cache(1, 1, D, 64)
+    ot.append(np.ascontiguousarray(d["K"][:, W * 64:]), np.ascontiguousarray(d["V"][:, W * 64:]), 0)
+    g = to_oracle(c)
+    kc = g.k_codes[0, 0, :n_full * 64].reshape(n_full, 64, D // 4)
+    vp = g.v_params[0, 0, :n_full * 64].reshape(n_full, 64, D // 32)
+    for j, oj in enumerate(types):
+        assert np.all(kc[j::W] == oj.k_codes[0, 0, :64]), f"k_codes of copies of window {j}"
+        assert np.all(g.k_params[0, 0, j:n_full:W] == oj.k_params[0, 0, 0]), f"k_params of window {j}"
+        assert np.all(g.v_codes[0, 0, j:n_full:W] == oj.v_codes[0, 0, 0]), f"v_codes of window {j}"
+        assert np.all(vp[j::W] == oj.v_params[0, 0, :64]), f"v_params of window {j}"
+    assert np.array_equal(g.k_tail[0, 0, :rem], ot.k_tail[0, 0, :rem]), "k_tail"
+    assert np.array_equal(g.v_params[0, 0, n_full * 64:T], ot.v_params[0, 0, :rem]), "tail v_params"
+    bits = np.zeros(128, np.uint8)
+    bits[:2 * rem] = 1
+    mask = np.packbits(bits.reshape(16, 8)[:, ::-1], axis=1).reshape(16)
+    assert np.array_equal(g.v_codes[0, 0, n_full] & mask, ot.v_codes[0, 0, 0] & mask), "tail v_codes"
+    del g, kc, vp
+
+    counts = [len(range(j, n_full, W)) for j in range(W)]
+    scale = 1 / math.sqrt(D)
+
+    def reference(q64):                      # q64 [1][Lq][Hq][D]
+        parts = [oj.attention(q64, 64, scale) for oj in types] + [ot.attention(q64, rem, scale)]
+        Lq = q64.shape[1]
+        out = np.empty((Lq, Hq, D))
+        lse = np.empty((Hq, Lq))
+        for r in range(Lq):
+            for hq in range(Hq):
+                m = np.array([p[1][0, hq, r] for p in parts]) + np.log(np.array(counts + [1.0]))
+                o = np.stack([p[0][0, r, hq] for p in parts])
+                out[r, hq], lse[hq, r] = oracle.merge(m, np.ones(W + 1), o)
+        return out, lse
+
+    q64 = synth.bf16_bits_to_f32(d["q"]).astype(np.float64)          # [1][Hq][D]
+    ref, rlse = reference(q64.reshape(1, 1, Hq, D))
+    lse = torch.empty(Hq, dtype=torch.float32, device="cuda")
+    out = kv.attn_int2_decode(c, T, dev_bf16(d["q"]), scale, lse=lse)
+    torch.cuda.synchronize()
+    err = np.abs(out.cpu().numpy()[0].astype(np.float64) - ref[0]).max()
+    assert err <= TOL, f"decode: max err {err:.3e}"
+    assert np.abs(lse.cpu().numpy() - rlse[:, 0]).max() < 1e-3, "decode lse"
+    # chunk attention: the query, its negation and its channel reversal
+    qc = np.stack([d["q"][0], d["q"][0] ^ 0x8000, d["q"][0, :, ::-1]])[None]   # [1][3][Hq][D]
+    qc = np.ascontiguousarray(qc)
+    ref, rlse = reference(synth.bf16_bits_to_f32(qc).astype(np.float64))
+    lse = torch.empty((1, Hq, 3), dtype=torch.float32, device="cuda")
+    out = kv.attn_int2_chunk(c, T, dev_bf16(qc), scale, lse=lse)
+    torch.cuda.synchronize()
+    err = np.abs(out.cpu().numpy()[0].astype(np.float64) - ref).max()
+    assert err <= TOL, f"chunk: max err {err:.3e}"
+    assert np.abs(lse.cpu().numpy()[0] - rlse).max() < 1e-3, "chunk lse"
