@@ -238,55 +238,72 @@ def test_window_prefix_and_rewind():
     _decode_check(c, o2, T, qd, q64, scale, "after the rewind")
 
 
-@pytest.mark.slow
-def test_decode_and_chunk_at_maximum_capacity():
-    """The largest capacity a cache takes (2^24 tokens per sequence and
-    head), filled by one append: 262,143 full windows, window w a copy of
-    window w % 7 of seven distinct ones, then a 17-token tail.  Every
-    window's cache bytes equal the oracle's for its copy, and decode (MFMA
-    path, 8,192 splits) and chunk attention over all 2^24 - 47 tokens equal
+def _small_like(c: kv.KVCache, cap: int = 64) -> oracle.Cache:
+    """An empty one-sequence, one-head oracle cache of capacity cap with the
+    modes and calibration inputs of c (itself one sequence and head)."""
+    L = c.layout
+    o = oracle.Cache(1, 1, L.head_dim, cap, L.key_mode, L.value_mode, L.n_centroids, L.qsac_topk,
+                     L.psac_rank, L.qsac_score, L.psac_format)
+    for name in ("centroids", "sens_w", "psac_basis"):
+        if getattr(c, name) is not None:
+            getattr(o, name)[:] = getattr(c, name).cpu().numpy()
+    return o
+
+
+def _maximum_capacity_check(c, d, q_dec, q_chunk, tag):
+    """Fills c (capacity 2^24, one sequence and kv head) in one append with
+    2^24 - 47 tokens: 262,143 full windows, window w a copy of window w % 7
+    of the seven in d, then d's last 17 tokens.  Every window's cache bytes
+    must equal the oracle's for its copy, and decode (q_dec bf16 bits
+    [1][Hq][D]) and chunk attention (q_chunk [1][Lq][Hq][D]) over all tokens
     the oracle's merge of the seven window attentions, each weighted by its
     number of copies, and the tail's."""
-    W, D, Hq = 7, 128, 4
-    T = (1 << 24) - 47
+    W, L = 7, c.layout
+    D, T = L.head_dim, (1 << 24) - 47
     n_full, rem = T // 64, T % 64
-    d = synth.llm_decode(B=1, Hkv=1, Hq=Hq, D=D, T=W * 64 + rem)
     t = np.arange(T)
     w = t // 64
     src = torch.from_numpy(np.where(w < n_full, (w % W) * 64 + t % 64, W * 64 + t - n_full * 64)).cuda()
     del t, w
-    c = kv.KVCache(1, 1, D, 1 << 24)
     kv.kv_quantize_append(c, dev_bf16(d["K"])[:, src].contiguous(), dev_bf16(d["V"])[:, src].contiguous(), 0)
     torch.cuda.synchronize()
     del src
     torch.cuda.empty_cache()
-    # the oracle's cache of each distinct window, and of the tail alone
     types = []
     for j in range(W):
-        oj = oracle.Cache(1, 1, D, 64)
+        oj = _small_like(c)
         oj.append(np.ascontiguousarray(d["K"][:, 64 * j:64 * j + 64]),
                   np.ascontiguousarray(d["V"][:, 64 * j:64 * j + 64]), 0)
         types.append(oj)
-    ot = oracle.Cache(1, 1, D, 64)
+    ot = _small_like(c)
     ot.append(np.ascontiguousarray(d["K"][:, W * 64:]), np.ascontiguousarray(d["V"][:, W * 64:]), 0)
     g = to_oracle(c)
-    kc = g.k_codes[0, 0, :n_full * 64].reshape(n_full, 64, D // 4)
-    vp = g.v_params[0, 0, :n_full * 64].reshape(n_full, 64, D // 32)
-    for j, oj in enumerate(types):
-        assert np.all(kc[j::W] == oj.k_codes[0, 0, :64]), f"k_codes of copies of window {j}"
-        assert np.all(g.k_params[0, 0, j:n_full:W] == oj.k_params[0, 0, 0]), f"k_params of window {j}"
-        assert np.all(g.v_codes[0, 0, j:n_full:W] == oj.v_codes[0, 0, 0]), f"v_codes of window {j}"
-        assert np.all(vp[j::W] == oj.v_params[0, 0, :64]), f"v_params of window {j}"
-    assert np.array_equal(g.k_tail[0, 0, :rem], ot.k_tail[0, 0, :rem]), "k_tail"
-    assert np.array_equal(g.v_params[0, 0, n_full * 64:T], ot.v_params[0, 0, :rem]), "tail v_params"
+    if L.key_mode == kv.KEY_WINDOW:
+        per_token, per_window = ["k_codes", "v_params"], ["k_params", "v_codes"]
+        assert np.array_equal(g.k_tail[0, 0, :rem], ot.k_tail[0, 0, :rem]), f"{tag}: k_tail"
+    else:
+        per_token, per_window = ["k_idx", "k_codes", "k_params", "v_params"], ["v_codes"]
+        if L.psac_rank > 0:
+            per_token += ["k_psac8", "k_psac_sc"] if L.psac_format == kv.PSAC_INT8 else ["k_psac"]
+    for name in per_token:
+        a = getattr(g, name)[0, 0]
+        rows = a[:n_full * 64].reshape((n_full, 64) + a.shape[1:])
+        for j, oj in enumerate(types):
+            assert np.all(rows[j::W] == getattr(oj, name)[0, 0, :64]), f"{tag}: {name} of copies of window {j}"
+        assert np.array_equal(a[n_full * 64:T], getattr(ot, name)[0, 0, :rem]), f"{tag}: {name} of the tail"
+    for name in per_window:
+        a = getattr(g, name)[0, 0]
+        for j, oj in enumerate(types):
+            assert np.all(a[j:n_full:W] == getattr(oj, name)[0, 0, 0]), f"{tag}: {name} of window {j}"
     bits = np.zeros(128, np.uint8)
     bits[:2 * rem] = 1
     mask = np.packbits(bits.reshape(16, 8)[:, ::-1], axis=1).reshape(16)
-    assert np.array_equal(g.v_codes[0, 0, n_full] & mask, ot.v_codes[0, 0, 0] & mask), "tail v_codes"
-    del g, kc, vp
+    assert np.array_equal(g.v_codes[0, 0, n_full] & mask, ot.v_codes[0, 0, 0] & mask), f"{tag}: tail v_codes"
+    del g
 
     counts = [len(range(j, n_full, W)) for j in range(W)]
     scale = 1 / math.sqrt(D)
+    Hq = q_dec.shape[1]
 
     def reference(q64):                      # q64 [1][Lq][Hq][D]
         parts = [oj.attention(q64, 64, scale) for oj in types] + [ot.attention(q64, rem, scale)]
@@ -300,21 +317,38 @@ def test_decode_and_chunk_at_maximum_capacity():
                 out[r, hq], lse[hq, r] = oracle.merge(m, np.ones(W + 1), o)
         return out, lse
 
-    q64 = synth.bf16_bits_to_f32(d["q"]).astype(np.float64)          # [1][Hq][D]
-    ref, rlse = reference(q64.reshape(1, 1, Hq, D))
+    ref, rlse = reference(synth.bf16_bits_to_f32(q_dec).astype(np.float64).reshape(1, 1, Hq, D))
     lse = torch.empty(Hq, dtype=torch.float32, device="cuda")
-    out = kv.attn_int2_decode(c, T, dev_bf16(d["q"]), scale, lse=lse)
+    out = kv.attn_int2_decode(c, T, dev_bf16(q_dec), scale, lse=lse)
     torch.cuda.synchronize()
     err = np.abs(out.cpu().numpy()[0].astype(np.float64) - ref[0]).max()
-    assert err <= TOL, f"decode: max err {err:.3e}"
-    assert np.abs(lse.cpu().numpy() - rlse[:, 0]).max() < 1e-3, "decode lse"
-    # chunk attention: the query, its negation and its channel reversal
-    qc = np.stack([d["q"][0], d["q"][0] ^ 0x8000, d["q"][0, :, ::-1]])[None]   # [1][3][Hq][D]
-    qc = np.ascontiguousarray(qc)
-    ref, rlse = reference(synth.bf16_bits_to_f32(qc).astype(np.float64))
-    lse = torch.empty((1, Hq, 3), dtype=torch.float32, device="cuda")
-    out = kv.attn_int2_chunk(c, T, dev_bf16(qc), scale, lse=lse)
+    assert err <= TOL, f"{tag}: decode max err {err:.3e}"
+    assert np.abs(lse.cpu().numpy() - rlse[:, 0]).max() < 1e-3, f"{tag}: decode lse"
+    Lq = q_chunk.shape[1]
+    ref, rlse = reference(synth.bf16_bits_to_f32(q_chunk).astype(np.float64))
+    lse = torch.empty((1, Hq, Lq), dtype=torch.float32, device="cuda")
+    out = kv.attn_int2_chunk(c, T, dev_bf16(q_chunk), scale, lse=lse)
     torch.cuda.synchronize()
     err = np.abs(out.cpu().numpy()[0].astype(np.float64) - ref).max()
-    assert err <= TOL, f"chunk: max err {err:.3e}"
-    assert np.abs(lse.cpu().numpy()[0] - rlse).max() < 1e-3, "chunk lse"
+    assert err <= TOL, f"{tag}: chunk max err {err:.3e}"
+    assert np.abs(lse.cpu().numpy()[0] - rlse).max() < 1e-3, f"{tag}: chunk lse"
+
+
+@pytest.mark.slow
+def test_window_keys_at_maximum_capacity():
+    """Window keys, 4 query heads per kv head (the MFMA decode, 8,192
+    splits): the query, its negation and its channel reversal as chunk rows."""
+    d = synth.llm_decode(B=1, Hkv=1, Hq=4, D=128, T=7 * 64 + 17)
+    qc = np.ascontiguousarray(np.stack([d["q"][0], d["q"][0] ^ 0x8000, d["q"][0, :, ::-1]])[None])
+    _maximum_capacity_check(kv.KVCache(1, 1, 128, 1 << 24), d, d["q"], qc, "window keys")
+
+
+@pytest.mark.slow
+def test_centroid_keys_at_maximum_capacity():
+    """64 centroids with the QSAC choice, rank-8 PSAC and rotated values,
+    calibrated on the seven distinct windows (two k-means rounds)."""
+    d = synth.sensitivity_aware(H=1, T=7 * 64 + 17, Lq=3, C=64, n_cal=256)
+    c = kv.KVCache(1, 1, 128, 1 << 24, key_mode=kv.KEY_CENTROID_QSAC, n_centroids=64, qsac_topk=4,
+                   psac_rank=8, value_mode=kv.VAL_HADAMARD)
+    calibrate(c, d["K"], d["kmeans_init"], 2, d["q_cal"])
+    _maximum_capacity_check(c, d, np.ascontiguousarray(d["q"][:, 0]), d["q"], "centroid keys")
