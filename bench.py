@@ -7,7 +7,7 @@ Default line (LLM-style decode): batch 16, 32 query heads / 8 KV heads (GQA
 token per sequence), resident in HBM before timing starts.
 
 One step = kv_quantize_append of the whole 32768-token context of every
-sequence, a 512 MiB write that evicts the 256 MB Infinity Cache, then
+sequence, a 512 MiB read that evicts the 256 MB Infinity Cache, then
 attn_int2_decode of the new query against the packed cache.  `value` is the
 decode's effective bandwidth: its algorithmic bytes (packed cache + query
 read, output written) over the median of its per-call HIP-event times
@@ -19,14 +19,16 @@ the oracle timed on the host cores on a bounded sample:
   toy          -- head_dim 64, 512 tokens, one head: decode and append latency;
   video_chunk  -- 40 heads, 4680 query rows against 31200 cached tokens of
                   256-centroid keys (4 GPU k-means rounds from the seeded
-                  picks) and rotated values, plus the append of the chunk;
+                  picks) and rotated values, plus the append of the chunk and
+                  the quantisation of the whole 31200-token history;
   long_history -- 40 heads, 1560 query rows against 93600 window-key tokens,
                   plus the append of the new 1560-token frame, and the
                   quantisation of the whole 93600-token history;
   sensitivity  -- 40 heads, 1560 query rows against 65536 tokens of QSAC
                   top-4 centroid keys with rank-8 PSAC (centroids from 4
                   k-means rounds; weights and principal directions from the
-                  1024 calibration queries).
+                  1024 calibration queries), and the quantisation of the whole
+                  65536-token history (the QSAC choice and PSAC terms).
 Chunk rooflines are bf16/fp16 MFMA: 4 * q_len * n_tokens * head_dim * heads
 flops per call.
 
@@ -410,9 +412,9 @@ def chunk_leg(name: str, steps: int, warmup: int, history_quantize: bool = True)
           flush=True)
 
     rec = {"config": desc}
-    if history_quantize and name == "long_history":
-        # quantisation of the whole history (93600 tokens x 40 heads): the
-        # same call that built the cache, so the state is unchanged
+    if history_quantize:
+        # quantisation of the whole history (Tn tokens x 40 heads): the same
+        # call that built the cache, so the state is unchanged
         hist = lambda: kv.kv_quantize_append(cache, Kd, Vd, 0)
         for _ in range(warmup):
             hist()
@@ -423,11 +425,15 @@ def chunk_leg(name: str, steps: int, warmup: int, history_quantize: bool = True)
             evs[i][1].record()
         torch.cuda.synchronize()
         sh = _stats([e[0].elapsed_time(e[1]) * 1e-3 for e in evs])
-        hbytes = Tn * H * (2 * D * 2 + D // 4 + D // 4 + (D // 32) * 4) + (Tn // 64) * H * D * 4
-        rec["quantize_history"] = dict(sh, tokens=Tn, mtok_s=round(Tn / (sh["median_us"] * 1e-6) / 1e6, 1),
-                                       effective_gbs=round(hbytes / (sh["median_us"] * 1e-6) / 1e9, 1),
-                                       pct_hbm_peak=round(100 * hbytes / (sh["median_us"] * 1e-6) / 1e9
-                                                          / HBM_PEAK_GBS, 2), bytes=hbytes)
+        rec["quantize_history"] = dict(sh, tokens=Tn, mtok_s=round(Tn / (sh["median_us"] * 1e-6) / 1e6, 1))
+        if name == "long_history":   # window keys: bound by HBM
+            hbytes = Tn * H * (2 * D * 2 + D // 4 + D // 4 + (D // 32) * 4) + (Tn // 64) * H * D * 4
+            rec["quantize_history"].update(
+                effective_gbs=round(hbytes / (sh["median_us"] * 1e-6) / 1e9, 1),
+                pct_hbm_peak=round(100 * hbytes / (sh["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+                bytes=hbytes)
+        else:                        # centroid keys: the assignment's arithmetic
+            rec["quantize_history"]["keys"] = desc["keys"]
 
     def step(ev=None):
         if tail0 is not None:
