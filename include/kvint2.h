@@ -346,11 +346,12 @@ size_t attn_int2_chunk_workspace(const kvq_layout* L, int32_t q_len,
  * [B][q_len][q_heads][D] in out_dtype; lse_dev (nullable) f32
  * [B][q_heads][q_len].  Every query row sees every cached token (no mask);
  * the chunk's own keys/values are not included -- merge them with lse.
- * Precision: fp16 MFMA operands with fp32 accumulation.  Every key enters
- * as fp16 hi + lo (exact to fp32), the PSAC term as hi/lo parts too; a
- * value enters as (code - 1) s, exact in fp16, with z + s of its group
- * summed exactly by one more MFMA; probabilities are fp16 (their rounding
- * multiplies v - o).  Within 2e-3 of the exact attention for keys with
+ * Precision: fp16 MFMA operands with fp32 accumulation.  A window key
+ * enters as (code - 1) s, exact in fp16, with its channels' z + s added to
+ * each row as a bias; a centroid key (centroid + residual, fp32) as fp16
+ * hi + lo, the PSAC term as hi/lo parts too; a value as (code - 1) s, exact
+ * in fp16, with z + s of its group summed exactly by one more MFMA;
+ * probabilities are fp16 (their rounding multiplies v - o).  Within 2e-3 of the exact attention for keys with
  * per-channel scales to 5 and values with peaks near 12 (the tests).
  * Same window-key contract on n_tokens and same errors as
  * attn_int2_decode. */
