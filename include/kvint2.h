@@ -143,8 +143,8 @@ typedef struct kvq_layout {
   int32_t qsac_score;  /* KVQ_QSAC_* (QSAC only; else ignored)         */
   int32_t psac_format; /* KVQ_PSAC_* (psac_rank > 0; else ignored)     */
   int32_t centroid_key_split; /* 0 or 1, accepted and ignored: chunk
-                         attention enters every key as fp16 hi + lo (kept
-                         for layout compatibility)                     */
+                         attention enters every centroid key as fp16
+                         hi + lo (kept for layout compatibility)       */
   int32_t n_modalities; /* M, 1..3 (KVQ_VAL_HADAMARD_MODAL; else ignored) */
 } kvq_layout;
 
@@ -351,10 +351,10 @@ size_t attn_int2_chunk_workspace(const kvq_layout* L, int32_t q_len,
  * each row as a bias; a centroid key (centroid + residual, fp32) as fp16
  * hi + lo, the PSAC term as hi/lo parts too; a value as (code - 1) s, exact
  * in fp16, with z + s of its group summed exactly by one more MFMA;
- * probabilities are fp16 (their rounding multiplies v - o).  Within 2e-3 of the exact attention for keys with
- * per-channel scales to 5 and values with peaks near 12 (the tests).
- * Same window-key contract on n_tokens and same errors as
- * attn_int2_decode. */
+ * probabilities are fp16 (their rounding multiplies v - o).  Within 2e-3
+ * of the exact attention for keys with per-channel scales to 5 and values
+ * with peaks near 12 (the tests).  Same window-key contract on n_tokens
+ * and same errors as attn_int2_decode. */
 int attn_int2_chunk(const kvq_cache* cache, int32_t n_tokens,
                     const void* q_bf16_dev, int32_t q_len, int32_t q_heads,
                     float scale, void* out_dev, int32_t out_dtype,
