@@ -11,6 +11,7 @@ import bit_kv_cache_int2_amd as kv
 import oracle
 import synth
 from gpu_helpers import TOL, assert_cache_equal, calibrate, dev_bf16, oracle_like, to_oracle
+from test_gpu_top1 import _exact_logits
 
 pytestmark = pytest.mark.gpu
 
@@ -254,10 +255,11 @@ def _maximum_capacity_check(c, d, q_dec, q_chunk, tag):
     """Fills c (capacity 2^24, one sequence and kv head) in one append with
     2^24 - 47 tokens: 262,143 full windows, window w a copy of window w % 7
     of the seven in d, then d's last 17 tokens.  Every window's cache bytes
-    must equal the oracle's for its copy, and decode (q_dec bf16 bits
+    must equal the oracle's for its copy, decode (q_dec bf16 bits
     [1][Hq][D]) and chunk attention (q_chunk [1][Lq][Hq][D]) over all tokens
     the oracle's merge of the seven window attentions, each weighted by its
-    number of copies, and the tail's."""
+    number of copies, and the tail's, and the top-1 token of each chunk row
+    the first copy of the oracle's choice."""
     W, L = 7, c.layout
     D, T = L.head_dim, (1 << 24) - 47
     n_full, rem = T // 64, T % 64
@@ -332,6 +334,32 @@ def _maximum_capacity_check(c, d, q_dec, q_chunk, tag):
     err = np.abs(out.cpu().numpy()[0].astype(np.float64) - ref).max()
     assert err <= TOL, f"{tag}: chunk max err {err:.3e}"
     assert np.abs(lse.cpu().numpy()[0] - rlse).max() < 1e-3, f"{tag}: chunk lse"
+    # top-1 token of the chunk rows: the copies of a window have bit-identical
+    # fp32 logits, so the first-on-ties rule must pick a token of the first
+    # copy (or of the tail); checked against the oracle over the 7 * 64 + 17
+    # distinct tokens as in test_gpu_top1
+    nd = W * 64 + rem
+    od = _small_like(c, 512)
+    od.append(np.ascontiguousarray(d["K"]), np.ascontiguousarray(d["V"]), 0)
+    idx, lg = kv.attn_int2_top1(c, T, dev_bf16(q_chunk), logits=True)
+    torch.cuda.synchronize()
+    idx, lg = idx.cpu().numpy()[0], lg.cpu().numpy()[0]             # [Hq][Lq]
+    q64 = synth.bf16_bits_to_f32(q_chunk).astype(np.float64)        # [1][Lq][Hq][D]
+    oi, _ = od.top1(q64, nd)
+    to_full = lambda t: t if t < W * 64 else n_full * 64 + t - W * 64
+    G = Hq // L.kv_heads
+    for hq in range(Hq):
+        ex, mag = _exact_logits(od, 0, hq // G, nd, q64[0, :, hq])
+        for r in range(Lq):
+            j = int(idx[hq, r])
+            assert j < W * 64 or n_full * 64 <= j < T, f"{tag}: top-1 {j} is a later copy"
+            t = j if j < W * 64 else W * 64 + j - n_full * 64
+            tol = 1e-5 * mag[r, t] + 1e-6
+            assert abs(lg[hq, r] - ex[r, t]) <= tol, f"{tag} hq={hq} r={r}: top-1 logit"
+            assert ex[r, t] >= ex[r].max() - 2 * tol - 1e-5 * mag[r].max(), f"{tag}: not a maximum"
+            srt = np.sort(ex[r])
+            if srt[-1] - srt[-2] > 2e-5 * mag[r].max() + 2e-6:
+                assert j == to_full(int(oi[0, hq, r])), f"{tag} hq={hq} r={r}: {j} vs the oracle"
 
 
 @pytest.mark.slow
