@@ -244,14 +244,17 @@ def _small_like(c: kv.KVCache, cap: int = 64) -> oracle.Cache:
     modes and calibration inputs of c (itself one sequence and head)."""
     L = c.layout
     o = oracle.Cache(1, 1, L.head_dim, cap, L.key_mode, L.value_mode, L.n_centroids, L.qsac_topk,
-                     L.psac_rank, L.qsac_score, L.psac_format)
+                     L.psac_rank, L.qsac_score, L.psac_format,
+                     M=L.n_modalities if L.value_mode == kv.VAL_HADAMARD_MODAL else 1)
     for name in ("centroids", "sens_w", "psac_basis"):
         if getattr(c, name) is not None:
             getattr(o, name)[:] = getattr(c, name).cpu().numpy()
+    if c.v_signs is not None:
+        o.v_signs[:] = c.v_signs.cpu().numpy().view(np.uint32)
     return o
 
 
-def _maximum_capacity_check(c, d, q_dec, q_chunk, tag):
+def _maximum_capacity_check(c, d, q_dec, q_chunk, tag, modal=None):
     """Fills c (capacity 2^24, one sequence and kv head) in one append with
     2^24 - 47 tokens: 262,143 full windows, window w a copy of window w % 7
     of the seven in d, then d's last 17 tokens.  Every window's cache bytes
@@ -259,7 +262,8 @@ def _maximum_capacity_check(c, d, q_dec, q_chunk, tag):
     [1][Hq][D]) and chunk attention (q_chunk [1][Lq][Hq][D]) over all tokens
     the oracle's merge of the seven window attentions, each weighted by its
     number of copies, and the tail's, and the top-1 token of each chunk row
-    the first copy of the oracle's choice."""
+    the first copy of the oracle's choice.  modal (per-modality rotations):
+    the modality of each of d's tokens, copied with them."""
     W, L = 7, c.layout
     D, T = L.head_dim, (1 << 24) - 47
     n_full, rem = T // 64, T % 64
@@ -267,17 +271,25 @@ def _maximum_capacity_check(c, d, q_dec, q_chunk, tag):
     w = t // 64
     src = torch.from_numpy(np.where(w < n_full, (w % W) * 64 + t % 64, W * 64 + t - n_full * 64)).cuda()
     del t, w
+    if modal is not None:
+        c.v_modality[0, :T] = torch.from_numpy(modal).cuda()[src]
     kv.kv_quantize_append(c, dev_bf16(d["K"])[:, src].contiguous(), dev_bf16(d["V"])[:, src].contiguous(), 0)
     torch.cuda.synchronize()
     del src
     torch.cuda.empty_cache()
+    def small(lo, hi, cap=64):    # d's tokens [lo, hi) in a cache of their own
+        o = _small_like(c, cap)
+        if modal is not None:
+            o.v_modal[0, :hi - lo] = modal[lo:hi]
+        return o
+
     types = []
     for j in range(W):
-        oj = _small_like(c)
+        oj = small(64 * j, 64 * j + 64)
         oj.append(np.ascontiguousarray(d["K"][:, 64 * j:64 * j + 64]),
                   np.ascontiguousarray(d["V"][:, 64 * j:64 * j + 64]), 0)
         types.append(oj)
-    ot = _small_like(c)
+    ot = small(W * 64, W * 64 + rem)
     ot.append(np.ascontiguousarray(d["K"][:, W * 64:]), np.ascontiguousarray(d["V"][:, W * 64:]), 0)
     g = to_oracle(c)
     if L.key_mode == kv.KEY_WINDOW:
@@ -339,7 +351,7 @@ def _maximum_capacity_check(c, d, q_dec, q_chunk, tag):
     # copy (or of the tail); checked against the oracle over the 7 * 64 + 17
     # distinct tokens as in test_gpu_top1
     nd = W * 64 + rem
-    od = _small_like(c, 512)
+    od = small(0, nd, 512)
     od.append(np.ascontiguousarray(d["K"]), np.ascontiguousarray(d["V"]), 0)
     idx, lg = kv.attn_int2_top1(c, T, dev_bf16(q_chunk), logits=True)
     torch.cuda.synchronize()
@@ -380,3 +392,17 @@ def test_centroid_keys_at_maximum_capacity():
                    psac_rank=8, value_mode=kv.VAL_HADAMARD)
     calibrate(c, d["K"], d["kmeans_init"], 2, d["q_cal"])
     _maximum_capacity_check(c, d, np.ascontiguousarray(d["q"][:, 0]), d["q"], "centroid keys")
+
+
+@pytest.mark.slow
+def test_modal_values_at_maximum_capacity():
+    """Window keys with values rotated per modality (three modalities in
+    runs across the seven windows and the tail)."""
+    d = synth.llm_decode(B=1, Hkv=1, Hq=4, D=128, T=7 * 64 + 17)
+    rng = np.random.default_rng(31)
+    c = kv.KVCache(1, 1, 128, 1 << 24, value_mode=kv.VAL_HADAMARD_MODAL, n_modalities=3)
+    signs = rng.integers(0, 1 << 32, size=(1, 3, 4), dtype=np.uint64).astype(np.uint32)
+    c.v_signs.copy_(torch.from_numpy(signs.view(np.int32)))
+    modal = np.repeat(rng.integers(0, 3, 465 // 15 + 1), 15)[:465].astype(np.uint8)
+    qc = np.ascontiguousarray(np.stack([d["q"][0], d["q"][0] ^ 0x8000, d["q"][0, :, ::-1]])[None])
+    _maximum_capacity_check(c, d, d["q"], qc, "modal values", modal)
