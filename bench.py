@@ -739,7 +739,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the path has no multi-GPU leg "
-              "(sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+              "(each GPU would hold whole heads or sequences of the cache); run with --gpus 1",
+              file=sys.stderr)
         return 2
     if args.workload == "copy":
         return copy_calibration(args.steps)
