@@ -375,12 +375,14 @@ def _maximum_capacity_check(c, d, q_dec, q_chunk, tag, modal=None):
 
 
 @pytest.mark.slow
-def test_window_keys_at_maximum_capacity():
-    """Window keys, 4 query heads per kv head (the MFMA decode, 8,192
-    splits): the query, its negation and its channel reversal as chunk rows."""
-    d = synth.llm_decode(B=1, Hkv=1, Hq=4, D=128, T=7 * 64 + 17)
+@pytest.mark.parametrize("D,Hq", [(128, 4), (64, 2)])
+def test_window_keys_at_maximum_capacity(D, Hq):
+    """Window keys: head_dim 128 with 4 query heads per kv head (the MFMA
+    decode, 8,192 splits) and head_dim 64 with 2 (the VALU decode); the
+    query, its negation and its channel reversal as chunk rows."""
+    d = synth.llm_decode(B=1, Hkv=1, Hq=Hq, D=D, T=7 * 64 + 17)
     qc = np.ascontiguousarray(np.stack([d["q"][0], d["q"][0] ^ 0x8000, d["q"][0, :, ::-1]])[None])
-    _maximum_capacity_check(kv.KVCache(1, 1, 128, 1 << 24), d, d["q"], qc, "window keys")
+    _maximum_capacity_check(kv.KVCache(1, 1, D, 1 << 24), d, d["q"], qc, f"window keys D={D}")
 
 
 @pytest.mark.slow
