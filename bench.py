@@ -30,7 +30,10 @@ the oracle timed on the host cores on a bounded sample:
                   1024 calibration queries), and the quantisation of the whole
                   65536-token history (the QSAC choice and PSAC terms).
 Chunk rooflines are bf16/fp16 MFMA: 4 * q_len * n_tokens * head_dim * heads
-flops per call.
+flops per call.  Every roofline also carries the fraction of the peak
+re-measured on the GPU in the same run (`peaks_measured`: an elementwise
+1 GiB kernel for HBM, an MFMA loop for the matrix cores) beside the vendor
+figure.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
     python bench.py --workload llm_decode|toy|video_chunk|long_history|sensitivity
@@ -145,6 +148,75 @@ def copy_calibration(steps: int) -> int:
     print(json.dumps({"workload": "copy", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
                       "launches": max(steps, 1)}), flush=True)
     return 0
+
+
+def measured_peaks() -> dict:
+    """The two roofline denominators re-measured on this GPU beside the
+    vendor figures: HBM by the plain elementwise kernel above over 1 GiB
+    (dst = ~src, 2 GiB moved per launch), dense fp16 MFMA by the library's
+    matrix-core probe (an MFMA loop on register operands, two blocks of
+    four waves per CU) and, for context, by a library GEMM (8192 x 8192 x
+    8192, torch.mm); medians of 20 per-call HIP-event times after 5 warm-up
+    calls."""
+    import numpy as np
+    import torch
+
+    import bit_kv_cache_int2_amd as kv
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for e0, e1 in evs:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e-3
+
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: torch.bitwise_not(src, out=dst))
+    del src, dst
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(n, n, device="cuda", dtype=torch.float16, generator=g)
+    b = torch.randn(n, n, device="cuda", dtype=torch.float16, generator=g)
+    c = torch.empty(n, n, device="cuda", dtype=torch.float16)
+    t_mm = timed(lambda: torch.mm(a, b, out=c))
+    del a, b, c
+    blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    probe_out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    flops = kv.mfma_peak_probe(blocks, 20000, probe_out)
+    t_loop = timed(lambda: kv.mfma_peak_probe(blocks, 20000, probe_out))
+    del probe_out
+    torch.cuda.empty_cache()
+    return {"hbm_gbs": round(2 * COPY_BYTES / t_copy / 1e9, 1),
+            "mfma_fp16_tflops": round(flops / t_loop / 1e12, 1),
+            "gemm_fp16_tflops": round(2.0 * n ** 3 / t_mm / 1e12, 1),
+            "method": "HBM: elementwise dst = ~src over 1 GiB (2 GiB moved); MFMA: an MFMA loop "
+                      "(v_mfma_f32_16x16x32_f16 on registers, 2 blocks of 4 waves per CU); GEMM: "
+                      "fp16 8192^3 torch.mm; medians of 20 HIP-event-timed calls"}
+
+
+def _generator_constants() -> dict:
+    import synth
+    return {"rng": "counter-based SplitMix64 per (seed, stream, index), fp64 Box-Muller normals, bf16 RNE",
+            "seed": f"{synth.SEED_BASE:#x} + workload number",
+            "streams": {"K": synth.S_K, "V": synth.S_V, "queries": synth.S_Q, "calibration queries": synth.S_QCAL,
+                        "k-means picks": synth.S_KMEANS, "per-channel key scales": synth.S_SIGMA,
+                        "query subspace": synth.S_SUBSPACE}}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ---------------------------------------------------------------- decode line
@@ -773,6 +845,18 @@ def main() -> int:
             legs[name], hosts[name] = chunk_leg(name, args.steps, args.warmup)
     rec, d = decode_leg(args.steps, args.warmup)
     rec.update(legs)
+    if args.workload == "all":
+        # the measured denominators beside the vendor peaks of each roofline
+        peaks = measured_peaks()
+        rec["peaks_measured"] = peaks
+        for r in [rec] + [v for v in legs.values() if isinstance(v, dict)]:
+            for key in ("roofline", "roofline_append"):
+                roof = r.get(key)
+                if isinstance(roof, dict):
+                    m = peaks["hbm_gbs"] if roof["bound"] == "hbm" else peaks["mfma_fp16_tflops"]
+                    roof["peak_measured"] = m
+                    roof["frac_of_measured"] = round(roof["achieved"] / m, 4)
+        rec["generator"] = _generator_constants()
     if with_cpu:
         t0 = time.perf_counter()
         rec["cpu_baseline"] = cpu_decode_baseline(d)
@@ -781,6 +865,10 @@ def main() -> int:
             rec["toy_single_head"]["cpu_baseline"] = cpu_toy_baseline(synth.toy_single_head())
         for name, host in hosts.items():
             rec[name]["cpu_baseline"] = cpu_chunk_baseline(name, host)
+        host_info = {"cpu_model": _cpu_model(), "nproc": os.cpu_count()}
+        for r in [rec] + [v for v in legs.values() if isinstance(v, dict)]:
+            if isinstance(r.get("cpu_baseline"), dict):
+                r["cpu_baseline"].update(host_info)
         print(f"oracle legs: {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
     print(json.dumps(rec), flush=True)
     return 0

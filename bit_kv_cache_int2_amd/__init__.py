@@ -94,6 +94,8 @@ def lib():
     L.attn_int2_chunk.restype = ctypes.c_int
     L.attn_int2_top1.argtypes = [pC, i32, vp, i32, i32, vp, vp, vp]
     L.attn_int2_top1.restype = ctypes.c_int
+    L.kvq_mfma_peak_probe.argtypes = [vp, i32, i32, vp]
+    L.kvq_mfma_peak_probe.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -373,3 +375,16 @@ def attn_int2_chunk(cache: KVCache, n_tokens: int, q: torch.Tensor, scale: float
                                  workspace.numel() * workspace.element_size(), _stream(stream)),
            "attn_int2_chunk")
     return out
+
+
+def mfma_peak_probe(blocks: int, iters: int, out: torch.Tensor = None, stream=None) -> float:
+    """Enqueues the matrix-core rate probe (include/kvprobe.h) and returns
+    the flops one launch performs; out: f32 device [blocks * 256]."""
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    _need_cuda(out, "out", torch.float32)
+    if out.numel() < blocks * 256:
+        raise ValueError(f"out must hold {blocks * 256} floats, got {out.numel()}")
+    _check(lib().kvq_mfma_peak_probe(_ptr(out), int(blocks), int(iters), _stream(stream)),
+           "kvq_mfma_peak_probe")
+    return float(blocks) * 4 * iters * 8 * 16384

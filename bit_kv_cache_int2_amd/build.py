@@ -25,7 +25,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 
-SOURCES = ["api.cpp", "quantize.hip", "assign.hip", "decode.hip", "chunk.hip", "top1.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "assign.hip", "decode.hip", "chunk.hip", "top1.hip", "peak.hip"]
 
 # Per-source extras for the attention kernels: MFMA accumulators in VGPRs
 # for decode (no copies between register files), and no NaN operands
@@ -34,6 +34,7 @@ SOURCES = ["api.cpp", "quantize.hip", "assign.hip", "decode.hip", "chunk.hip", "
 # quantizer takes finite keys and values, so its min/max chains need no
 # quieting of each converted input either.
 EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+         "peak.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],   # eight plain accumulator chains
          "chunk.hip": ["-fno-honor-nans"],
          "quantize.hip": ["-fno-honor-nans"]}
 

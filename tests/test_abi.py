@@ -1,8 +1,9 @@
-"""The C-ABI library loads, exports every function include/kvint2.h
-declares, and its host-side validation rejects bad arguments before any
-launch.  No call here reaches the GPU (validation fails first), so this runs
-on machines without one."""
+"""The C-ABI library loads, exports every function include/*.h declares,
+and its host-side validation rejects bad arguments before any launch.  No
+call here reaches the GPU (validation fails first), so this runs on machines
+without one."""
 import ctypes
+import glob
 import os
 import re
 
@@ -14,8 +15,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvint2.h")
 
 
-def _declared_functions():
-    src = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
     return sorted(set(names))
@@ -30,9 +31,21 @@ def test_header_declares_the_four_entry_points():
 
 def test_library_exports_every_declared_symbol():
     L = kv.lib()
-    for n in _declared_functions():
-        assert hasattr(L, n), n
+    headers = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
+    assert HEADER in headers
+    for h in headers:
+        for n in _declared_functions(h):
+            assert hasattr(L, n), f"{os.path.basename(h)}: {n}"
     assert L.kvq_status_string(-3) == b"exceeds cache capacity"
+
+
+def test_mfma_probe_validation_without_launch():
+    L = kv.lib()
+    p = ctypes.c_void_p(1 << 20)
+    assert L.kvq_mfma_peak_probe(None, 1, 1, None) == kv.KVQ_EINVAL
+    assert L.kvq_mfma_peak_probe(p, 0, 1, None) == kv.KVQ_EINVAL
+    assert L.kvq_mfma_peak_probe(p, 1, 0, None) == kv.KVQ_EINVAL
+    assert L.kvq_mfma_peak_probe(p, (1 << 20) + 1, 1, None) == kv.KVQ_EINVAL
 
 
 def _layout(**kw):
